@@ -1,0 +1,132 @@
+"""float64 CPU oracle for causal grouped-query attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The HIP library never imports, links or
+calls anything here, and nothing here imports the HIP library.
+
+Two independent implementations of one definition live in this package:
+
+* ``gqa_oracle.c`` (loaded here through ctypes): per-row materialized scores,
+  libm ``exp`` in float64, threads over independent (batch, head) units.
+* ``ref_numpy.py``: the same definition as whole-matrix NumPy float64 algebra.
+
+The definition (scores = scale * Q K^T, additive -inf causal mask, softmax over
+keys, times V; query head h reads K/V head h // (Hq // Hkv)) follows Riftco's
+"Causal Multi-Head Self-Attention" page ("Dataflow and shapes", "The causal
+mask"), the "Grouped-Query Attention" chapter (sections 5.1 and 5.2) and, for
+cached decode, makarna's ``CausalAttentionCached``: the new tokens sit at
+absolute positions startPos .. startPos+newTokens-1, each sees every cached key
+up to and including its own position, and the scale is 1/sqrt(headDim).
+
+Inputs are widened exactly to float64 (bf16 and fp32 values are all exactly
+representable), so the oracle never rounds an input.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gqa_oracle.c into liboracle.so with the host C compiler.
+
+    No -ffast-math: the oracle keeps IEEE float64 semantics.
+    """
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC", "-shared",
+               "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_attention.restype = ctypes.c_int
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_attention.argtypes = [dp, dp, dp, dp, dp,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                         ctypes.c_long, ctypes.c_int]
+        lib.oracle_default_threads.restype = ctypes.c_int
+        lib.oracle_default_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def to_f64(x) -> np.ndarray:
+    """Exact widening of a numpy array or torch tensor (fp32 / bf16 / fp64) to float64."""
+    if hasattr(x, "detach"):  # torch tensor: widen through torch, which is exact for bf16/fp32
+        import torch
+
+        x = x.detach().to("cpu", torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    return int(_load().oracle_default_threads())
+
+
+def attention(q, k, v, scale: float, causal: bool = True, pos0: int = 0,
+              nthreads: int = 0, want_probs: bool = False):
+    """Materialized float64 attention in head-major layout.
+
+    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d].  Query row i is at absolute
+    position pos0 + i.  Returns out [B, Hq, Tq, d] (float64), and P
+    [B, Hq, Tq, Tk] as well when want_probs.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (q.shape, k.shape, v.shape))
+    out = np.zeros((B, Hq, Tq, d), dtype=np.float64)
+    probs = np.zeros((B, Hq, Tq, Tk), dtype=np.float64) if want_probs else None
+    rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(probs),
+                                  B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)),
+                                  int(pos0), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments (rc=%d)" % rc)
+    return (out, probs) if want_probs else out
+
+
+def prefill(q, k, v, scale: float, causal: bool = True, nthreads: int = 0):
+    """Full-sequence prefill: q [B,Hq,T,d], k/v [B,Hkv,T,d] -> out [B,Hq,T,d]."""
+    return attention(q, k, v, scale, causal, 0, nthreads)
+
+
+def decode_cached(q, kcache, vcache, start_pos: int, nthreads: int = 0):
+    """Cached decode: q [B,n,Hq,d] (new tokens, token-major like makarna's Q),
+    kcache/vcache [B,Hkv,totalLen,d] already holding the new tokens at
+    start_pos..start_pos+n-1.  Scale is 1/sqrt(d) as in CausalAttentionCached.
+    Returns out [B,n,Hq,d] (float64).
+    """
+    qh = to_f64(q).transpose(0, 2, 1, 3)  # layout change only: [B,Hq,n,d]
+    d = qh.shape[-1]
+    out = attention(qh, kcache, vcache, 1.0 / math.sqrt(d), True, start_pos, nthreads)
+    return np.ascontiguousarray(out.transpose(0, 2, 1, 3))
+
+
+def probs(q, k, v, scale: float, causal: bool = True, pos0: int = 0):
+    """The probability matrix P [B,Hq,Tq,Tk] (small shapes only)."""
+    return attention(q, k, v, scale, causal, pos0, 1, want_probs=True)[1]
