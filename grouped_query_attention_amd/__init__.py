@@ -1,0 +1,140 @@
+"""Thin Python binding of libgqa_attn.so (causal grouped-query attention on gfx950).
+
+The functions mirror the C ABI in include/gqa_attn.h one for one and only marshal
+arguments: they check torch tensors' device, dtype, shape and contiguity, pass raw
+device pointers and the current HIP stream, and turn a negative status into an
+exception.  Every step of the computation runs in the library's HIP kernels; there
+is no fallback.  Importing this package fails if the library has not been built
+(``python grouped_query_attention_amd/build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa_attn.so")
+
+GQA_F32, GQA_BF16 = 0, 1
+GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_EHIP = 0, -1, -2, -3, -4
+GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
+
+# every symbol include/gqa_attn.h declares
+EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_decode_workspace_bytes",
+            "attn_decode_num_splits", "attn_decode_cached", "attn_strerror")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgqa_attn.so is not built (%s); run python grouped_query_attention_amd/build.py"
+                      % LIB_PATH)
+
+lib = ctypes.CDLL(LIB_PATH)
+_i, _vp, _f, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+lib.attn_prefill.restype = _i
+lib.attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+lib.attn_prefill_ex.restype = _i
+lib.attn_prefill_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]
+lib.attn_decode_workspace_bytes.restype = _sz
+lib.attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+lib.attn_decode_num_splits.restype = _i
+lib.attn_decode_num_splits.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+lib.attn_decode_cached.restype = _i
+lib.attn_decode_cached.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+lib.attn_strerror.restype = ctypes.c_char_p
+lib.attn_strerror.argtypes = [_i]
+
+
+class GQAError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__("%s: %s (status %d)" % (what, attn_strerror(code), code))
+
+
+def attn_strerror(code: int) -> str:
+    return lib.attn_strerror(int(code)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GQA_F32
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _dev_ptr(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def attn_prefill(q, k, v, scale=None, causal=True, out=None, algo=GQA_ALGO_AUTO, stream=None):
+    """Causal (or full) GQA prefill.  q [B,Hq,T,d]; k, v [B,Hkv,T,d] (same dtype,
+    float32 or bfloat16).  Returns out [B,Hq,T,d] float32 (written into `out` if given)."""
+    B, Hq, T, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Hkv, T, d] matching q %s; got %s %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32:
+        raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
+    rc = lib.attn_prefill_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                             B, Hq, Hkv, T, d, float(scale), int(bool(causal)), _dtype_code(q), int(algo),
+                             _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_prefill")
+    return out
+
+
+def attn_decode_workspace_bytes(B, new_tokens, total_len, Hq, Hkv, d, dtype=GQA_BF16) -> int:
+    return int(lib.attn_decode_workspace_bytes(B, new_tokens, total_len, Hq, Hkv, d, int(dtype)))
+
+
+def attn_decode_num_splits(B, new_tokens, total_len, Hq, Hkv, d, dtype=GQA_BF16) -> int:
+    return int(lib.attn_decode_num_splits(B, new_tokens, total_len, Hq, Hkv, d, int(dtype)))
+
+
+def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, stream=None):
+    """Cached decode.  q [B,n,Hq,d] (new tokens, token-major); kcache, vcache
+    [B,Hkv,L,d] holding positions 0..L-1 with the new tokens at start_pos..start_pos+n-1.
+    Scale is 1/sqrt(d).  Returns out [B,n,Hq,d] float32.  A workspace tensor of at least
+    attn_decode_workspace_bytes(...) bytes is allocated here when not supplied."""
+    B, n, Hq, d = q.shape
+    if kcache.dim() != 4 or kcache.shape[0] != B or kcache.shape[3] != d or vcache.shape != kcache.shape:
+        raise ValueError("kcache, vcache must be [B, Hkv, L, d]; got %s %s"
+                         % (tuple(kcache.shape), tuple(vcache.shape)))
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise TypeError("q, kcache, vcache must share one dtype")
+    Hkv, L = kcache.shape[1], kcache.shape[2]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32:
+        raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
+    need = attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.attn_decode_cached(_dev_ptr(q, "q"), _dev_ptr(kcache, "kcache"), _dev_ptr(vcache, "vcache"),
+                                _dev_ptr(out, "out"), n, L, int(start_pos), Hq, Hkv, d, B, dt,
+                                ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_decode_cached")
+    return out

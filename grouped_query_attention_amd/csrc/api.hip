@@ -1,0 +1,134 @@
+// api.hip -- the C ABI declared in include/gqa_attn.h: argument validation on the host,
+// kernel choice, and launch on the caller's stream.  Nothing here allocates, frees or
+// synchronizes.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "gqa_attn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxHeadDim = 256;
+constexpr long long kMaxSeq = 1LL << 30;
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int dtype, int B, int Hq, int Hkv, int d_h) {
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_EINVAL;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d_h <= 0) return GQA_EINVAL;
+  if (Hq % Hkv != 0) return GQA_EINVAL;
+  if (d_h > kMaxHeadDim) return GQA_EUNSUPPORTED;
+  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return GQA_EUNSUPPORTED;
+  return GQA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_EHIP; }
+
+int prefill_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                 int T, int d_h, float scale, int causal, int dtype, int algo, void* stream) {
+  int rc = check_common(dtype, B, Hq, Hkv, d_h);
+  if (rc != GQA_OK) return rc;
+  if (T < 0 || !isfinite(scale) || (causal != 0 && causal != 1)) return GQA_EINVAL;
+  if (algo != GQA_ALGO_AUTO && algo != GQA_ALGO_GENERIC && algo != GQA_ALGO_MFMA) return GQA_EINVAL;
+  if (T > kMaxSeq) return GQA_EUNSUPPORTED;
+  // an explicit kernel request is checked even for empty tensors, so a zero-size call
+  // tells the caller whether that kernel covers the shape
+  const bool mfma_ok = gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
+  if (algo == GQA_ALGO_MFMA && !mfma_ok) return GQA_EUNSUPPORTED;
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_EINVAL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (algo == GQA_ALGO_MFMA || (algo == GQA_ALGO_AUTO && mfma_ok)) {
+    gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal};
+    return status_of(gqa::launch_attn_prefill_mfma(a, s));
+  }
+  const long long sd = d_h;
+  gqa::GenericArgs a{q, k, v, out, dtype, B, Hq, Hkv, T, T, d_h, scale, causal, 0,
+                     (long long)Hq * T * sd, (long long)T * sd, sd};
+  return status_of(gqa::launch_attn_generic(a, s));
+}
+
+int decode_check(int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
+                 int dtype) {
+  int rc = check_common(dtype, B, Hq, Hkv, d_h);
+  if (rc != GQA_OK) return rc;
+  if (newTokens < 0 || totalLen < 0 || startPos < 0) return GQA_EINVAL;
+  if ((long long)startPos + newTokens > totalLen) return GQA_EINVAL;
+  if (totalLen > kMaxSeq) return GQA_EUNSUPPORTED;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                 int T, int d_h, float scale, int causal, int dtype, void* stream) {
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, dtype, GQA_ALGO_AUTO,
+                      stream);
+}
+
+int attn_prefill_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                    int Hkv, int T, int d_h, float scale, int causal, int dtype, int algo,
+                    void* stream) {
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, dtype, algo, stream);
+}
+
+size_t attn_decode_workspace_bytes(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
+                                   int dtype) {
+  if (decode_check(newTokens, totalLen, totalLen - newTokens, Hq, Hkv, d_h, B, dtype) != GQA_OK)
+    return 0;
+  if (B == 0 || newTokens == 0) return 0;
+  return gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype).workspace;
+}
+
+int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
+                           int dtype) {
+  if (decode_check(newTokens, totalLen, totalLen - newTokens, Hq, Hkv, d_h, B, dtype) != GQA_OK)
+    return 0;
+  if (B == 0 || newTokens == 0) return 0;
+  return gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype).nsplit;
+}
+
+int attn_decode_cached(const void* q, const void* kcache, const void* vcache, float* out,
+                       int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = decode_check(newTokens, totalLen, startPos, Hq, Hkv, d_h, B, dtype);
+  if (rc != GQA_OK) return rc;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return GQA_EINVAL;
+  const gqa::DecodePlan plan = gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype);
+  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+    return GQA_EWORKSPACE;
+  if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = 1.0f / sqrtf((float)d_h);
+  if (plan.mfma) {
+    gqa::DecodeArgs a{q, kcache, vcache, out, B, newTokens, Hq, Hkv, totalLen, d_h, startPos,
+                      scale, workspace};
+    return status_of(gqa::launch_attn_decode_mfma(a, plan, s));
+  }
+  const long long sd = d_h;
+  gqa::GenericArgs a{q, kcache, vcache, out, dtype, B, Hq, Hkv, newTokens, totalLen, d_h, scale,
+                     1, startPos, (long long)newTokens * Hq * sd, sd, (long long)Hq * sd};
+  return status_of(gqa::launch_attn_generic(a, s));
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case GQA_OK: return "success";
+    case GQA_EINVAL: return "invalid argument";
+    case GQA_EUNSUPPORTED: return "unsupported shape or dtype for the built kernels";
+    case GQA_EWORKSPACE: return "decode workspace missing or too small";
+    case GQA_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// launch.h -- internal interface between the C ABI (api.hip) and the kernels.
+// Not installed; the public interface is include/gqa_attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gqa {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// Generic vector-ALU kernel: q/out rows addressed by strides (elements), so one
+// kernel serves the head-major prefill layout and the token-major decode layout.
+// k, v are [B, Hkv, Tk, d].  Query row i is at absolute position pos0 + i.
+struct GenericArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  int dtype;
+  int B, Hq, Hkv, Tq, Tk, d;
+  float scale;
+  int causal;
+  int pos0;
+  long long q_sb, q_sh, q_st;  // strides of q and out: batch, head, row
+};
+hipError_t launch_attn_generic(const GenericArgs& a, hipStream_t stream);
+
+// bf16 matrix-core prefill: q/out [B,Hq,T,d], k/v [B,Hkv,T,d], d in {16,...,128} step 16.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  int B, Hq, Hkv, T, d;
+  float scale;
+  int causal;
+};
+bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv);
+hipError_t launch_attn_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+
+// Split-KV decode plan, a pure function of the shape.
+struct DecodePlan {
+  int nsplit;        // key chunks per (sequence, kv head); 1 = no split
+  int chunk;         // keys per chunk (multiple of the kernel's key tile)
+  size_t workspace;  // bytes of partial results
+  bool mfma;         // the bf16 matrix-core decode kernel applies
+};
+DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int dtype);
+
+struct DecodeArgs {
+  const void* q;   // [B, n, Hq, d]
+  const void* kc;  // [B, Hkv, L, d]
+  const void* vc;
+  float* out;      // [B, n, Hq, d]
+  int B, n, Hq, Hkv, L, d, start_pos;
+  float scale;
+  void* workspace;
+};
+hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,341 @@
+// prefill_mfma.hip -- bf16 matrix-core causal GQA prefill for gfx950.
+//
+// Computes, per query head h (K/V head g = h / G), out = softmax(scale * Q K^T + mask) V
+// with the causal mask of Hesper's "Causal Masking" section, as the memory-linear
+// online-softmax algorithm of Riftco's "Two exact full-sequence algorithms": running
+// row max and normalizer, numerator rescaled as key tiles arrive, no [T, T] buffer.
+//
+// Mapping onto CDNA4:
+//  * A workgroup owns one q-tile of 128 query rows for HPW query heads of the same
+//    K/V group (HPW = 2 when the group has an even number of heads) -- 4*HPW waves,
+//    each wave 32 rows of one head.  The K/V tile (64 keys) is staged once in LDS and
+//    read by every wave: the GQA reuse of "Grouped-Query Attention" section 5.1 lands
+//    in LDS, not in a repeat_interleave copy.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//    A = K rows straight from LDS, B = Q^T held in registers for the whole kernel.
+//    In the 32x32 accumulator every lane then holds 16 keys of ONE query, so row
+//    reductions are in-lane plus one permlane32 swap between the two lane halves.
+//  * The same accumulator, converted to bf16, is the B operand of O^T = V^T P^T: its
+//    lane holds keys {4h..4h+3, 8+4h..8+4h+3} (h = lane/32) of each 16-key step,
+//    which is a valid K-ordering as long as the A operand (V^T) uses the same one.
+//    ds_read_b64_tr_b16 reads four consecutive keys of one head-dim column out of the
+//    row-major V tile, so V never needs a transposed copy.
+//  * Online softmax in log2 units (scale*log2(e) folded into one FMA before
+//    v_exp_f32); the running max is only moved when it grows by more than 8, so the
+//    O rescale is skipped on almost every tile (values of p stay below 2^8).
+//  * Causal skipping: tiles (and 32-key halves of tiles) entirely above a wave's
+//    diagonal are not computed; the mask is only evaluated on diagonal tiles.
+//  * Heaviest q-tiles are dispatched first; blocks of one (batch, head group) keep
+//    the same block-id residue mod 8, i.e. stay on one XCD and share its L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace gqa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kBM = 128;        // query rows per head per workgroup
+constexpr int kBN = 64;         // keys per LDS tile
+constexpr float kLazyTau = 8.f; // log2 growth of the row max tolerated before rescaling
+
+template <int D>
+struct Geo {
+  static constexpr int kSteps = D / 16;           // K-steps of the S^T contraction
+  static constexpr int kDBlocks = (D + 31) / 32;  // 32-row blocks of O^T
+  // K rows: an odd number of 16-byte chunks apart, so 8 lanes reading the same
+  // column of 8 consecutive rows hit 8 different bank groups.
+  static constexpr int kKStride = 2 * D + 16;
+  // V rows: the transposed read touches 4 rows x 32 bytes per 16 lanes; a stride of
+  // 32 or 96 mod 128 bytes puts those 4 rows in distinct banks.  Rows are read up to
+  // the next multiple of 32 head dims (the padding feeds discarded O^T rows only).
+  static constexpr int kVRead = 64 * kDBlocks;
+  static constexpr int kVStride = kVRead + 32;
+  static constexpr int kKTile = kBN * kKStride;
+  static constexpr int kVTile = kBN * kVStride;
+  static constexpr int kLds = 2 * (kKTile + kVTile);  // double-buffered
+  static constexpr int kChunks = kBN * D / 8;          // 16-byte chunks per tile
+};
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int HPW>
+__global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ out, int Hq, int Hkv, int T, float c,
+    unsigned qsign, int causal, int n_qtiles, int n_hgroups, int B) {
+  using G_ = Geo<D>;
+  constexpr int NT = HPW * 256;
+  constexpr int NCH = (G_::kChunks + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) char smem[G_::kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;   // which 16-key half of each 32 the lane holds
+  const int col = lane & 31;    // query column of the lane in its wave's 32 rows
+
+  // block -> (q-tile, head group, batch): heaviest q-tiles first
+  const int per_qt = n_hgroups * B;
+  const int bid = blockIdx.x;
+  const int qt = n_qtiles - 1 - bid / per_qt;
+  const int rem = bid % per_qt;
+  const int hg = rem % n_hgroups;
+  const int b = rem / n_hgroups;
+  const int h = hg * HPW + wave / 4;
+  const int g = (hg * HPW) / (Hq / Hkv);
+  const int q0 = qt * kBM;
+  const int qw = q0 + (wave & 3) * 32;   // first query row of this wave
+  const int qi = qw + col;               // this lane's query row (absolute position)
+
+  const long long kv_base = ((long long)b * Hkv + g) * (long long)T * D;
+  const uint16_t* kg = k + kv_base;
+  const uint16_t* vg = v + kv_base;
+
+  // Q^T fragments: lane holds query qi, head dims 16*s + 8*half + 0..7
+  bf16x8 qf[G_::kSteps];
+  {
+    const uint16_t* qrow = q + (((long long)b * Hq + h) * T + qi) * D;
+#pragma unroll
+    for (int s = 0; s < G_::kSteps; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < T) x = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half);
+      x ^= qsign;  // negative scale: flip the sign of q exactly, use |scale|
+      qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 o[G_::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < G_::kDBlocks; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;  // running max, log2 units (same in both lane halves)
+  float l_part = 0.f;       // this lane's share of the normalizer
+
+  const int kend = causal ? min(T, q0 + kBM) : T;
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  // cooperative tile load: global -> registers -> LDS
+  u32x4 kreg[NCH], vreg[NCH];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = tid + i * NT;
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ch < G_::kChunks) {
+        const int row = ch / (D / 8), c16 = ch % (D / 8);
+        const int key = t * kBN + row;
+        if (key < T) {
+          kreg[i] = *reinterpret_cast<const u32x4*>(kg + (long long)key * D + c16 * 8);
+          vreg[i] = *reinterpret_cast<const u32x4*>(vg + (long long)key * D + c16 * 8);
+        }
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    char* kl = smem + buf * G_::kKTile;
+    char* vl = smem + 2 * G_::kKTile + buf * G_::kVTile;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = tid + i * NT;
+      if (ch < G_::kChunks) {
+        const int row = ch / (D / 8), c16 = ch % (D / 8);
+        *reinterpret_cast<u32x4*>(kl + row * G_::kKStride + c16 * 16) = kreg[i];
+        *reinterpret_cast<u32x4*>(vl + row * G_::kVStride + c16 * 16) = vreg[i];
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+
+    const int k0 = t * kBN;
+    // keys k0.. are all beyond this wave's last row: nothing to do (causal)
+    const bool active = !causal || k0 <= qw + 31;
+    if (active) {
+      const char* kl = smem + buf * G_::kKTile;
+      const char* vl = smem + 2 * G_::kKTile + buf * G_::kVTile;
+      // second 32-key half entirely above the diagonal?
+      const int nsb = (causal && k0 + 32 > qw + 31) ? 1 : 2;
+      const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
+
+      f32x16 s[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        s[sb] = f32x16{};
+        if (sb < nsb) {
+          const char* krow = kl + (sb * 32 + col) * G_::kKStride + half * 16;
+#pragma unroll
+          for (int st = 0; st < G_::kSteps; ++st) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + st * 32);
+            s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[sb], 0, 0, 0);
+          }
+        }
+      }
+
+      // mask (diagonal tiles only): key j of accumulator r is
+      // k0 + 32*sb + 8*(r/4) + 4*half + r%4
+      if (diag) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool ok = causal ? (j <= qi) : (j < T);
+            if (!ok || sb >= nsb) s[sb][r] = -INFINITY;
+          }
+      } else if (nsb == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[1][r] = -INFINITY;
+      }
+
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      if (nsb == 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      }
+      mx = pair_max(mx);
+      const float mt = mx * c;  // tile max in log2 units
+      const bool need = mt > m_run + kLazyTau;
+      if (__any(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < G_::kDBlocks; ++db) o[db] *= alpha;
+        m_run = m_new;
+      }
+
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (sb >= nsb) break;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m_run));
+          s[sb][r] = p;
+          l_part += p;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[sb][kk][e] = (__bf16)s[sb][8 * kk + e];
+      }
+
+      // O^T += V^T P^T.  Transposed-read addressing inside each 16-lane group:
+      // lane s reads 4 head dims (m0 + 4*(s%4) ..) of key row (k0p + s/4); after the
+      // transpose lane s holds head dim m0 + s of keys k0p .. k0p+3.
+      const int grp = lane >> 4, sl = lane & 15;
+      const int m0 = 16 * (grp & 1);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (sb < nsb) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int k0p = 32 * sb + 16 * kk + 4 * half;
+            const char* vrow = vl + (k0p + (sl >> 2)) * G_::kVStride + (m0 + 4 * (sl & 3)) * 2;
+#pragma unroll
+            for (int db = 0; db < G_::kDBlocks; ++db) {
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + db * 64));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(vrow + 8 * G_::kVStride + db * 64));
+              const bf16x8 a = __builtin_bit_cast(
+                  bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[sb][kk], o[db], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: O^T row (head dim) of accumulator r in block db is
+  // 32*db + 8*(r/4) + 4*half + r%4; column is this lane's query.
+  const float inv = 1.f / pair_sum(l_part);
+  if (qi < T) {
+    float* orow = out + (((long long)b * Hq + h) * T + qi) * D;
+#pragma unroll
+    for (int db = 0; db < G_::kDBlocks; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int dd = 32 * db + 8 * rq + 4 * half;
+        if (dd < D) {
+          f32x4 val = {o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv, o[db][4 * rq + 2] * inv,
+                       o[db][4 * rq + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + dd) = val;
+        }
+      }
+  }
+}
+
+template <int D, int HPW>
+hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
+  const int n_qtiles = (a.T + kBM - 1) / kBM;
+  const int n_hgroups = a.Hq / HPW;
+  const long long nblocks = (long long)n_qtiles * n_hgroups * a.B;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  float c = fabsf(a.scale) * 1.4426950408889634f;
+  // scale 0: every visible key gets the same weight; a tiny positive factor keeps the
+  // masked scores at -inf without changing any visible weight measurably
+  if (c == 0.f) c = 1e-30f;
+  const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW>), dim3((unsigned)nblocks), dim3(HPW * 256), 0,
+                     stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.out, a.Hq, a.Hkv, a.T, c, qsign, a.causal,
+                     n_qtiles, n_hgroups, a.B);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  if (G % 2 == 0) return launch_dh<D, 2>(a, stream);
+  return launch_dh<D, 1>(a, stream);
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv) {
+  return dtype == kBF16 && d > 0 && d <= 128 && d % 16 == 0 && Hkv > 0 && Hq % Hkv == 0;
+}
+
+hipError_t launch_attn_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 16: return launch_d<16>(a, stream);
+    case 32: return launch_d<32>(a, stream);
+    case 48: return launch_d<48>(a, stream);
+    case 64: return launch_d<64>(a, stream);
+    case 80: return launch_d<80>(a, stream);
+    case 96: return launch_d<96>(a, stream);
+    case 112: return launch_d<112>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gqa

@@ -1,0 +1,124 @@
+/*
+ * gqa_attn.h -- C ABI of the gfx950 (MI355X) causal grouped-query attention library
+ * (libgqa_attn.so).
+ *
+ * What every entry point computes, per batch b, query head h and query row i:
+ *
+ *   g     = h / (Hq / Hkv)        query heads are grouped over K/V heads the way
+ *                                 repeat_interleave(group_size) lays them out
+ *                                 ("Grouped-Query Attention", section 5.1)
+ *   p_i   = absolute position of query row i (i in prefill, startPos + i in decode)
+ *   s_ij  = scale * <q[b,h,i,:], k[b,g,j,:]>           (Riftco "Causal Multi-Head
+ *                                                      Self-Attention", "Dataflow and shapes")
+ *   P_ij  = softmax over j of s_ij, with every key j > p_i given probability exactly 0
+ *           when causal (Hesper "Attention" page, "Causal Masking")
+ *   out[b,h,i,:] = sum_j P_ij * v[b,g,j,:]
+ *
+ * Conventions shared by all entry points:
+ *   - Tensor pointers are DEVICE pointers on the current HIP device, owned by the
+ *     caller, contiguous row-major, and 16-byte aligned.  The library never allocates,
+ *     frees or synchronizes; inputs are read-only.
+ *   - dtype (enum gqa_dtype) is the element type of q, k, v (or q, kcache, vcache);
+ *     out is always float32.  Accumulation is float32 in both dtypes.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.  Work is
+ *     enqueued on it and the call returns before it completes.
+ *   - Arguments are validated on the host before anything is enqueued.  A bad argument
+ *     returns a negative status and enqueues nothing.  Sizes of zero (B, T, newTokens)
+ *     return GQA_OK and enqueue nothing.  GQA_EHIP reports a launch error; a fault
+ *     inside a kernel surfaces at the caller's next synchronization.
+ *   - Calls are re-entrant; concurrent decode calls need distinct workspaces.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 };
+
+enum gqa_status {
+    GQA_OK = 0,
+    GQA_EINVAL = -1,       /* argument outside the documented domain */
+    GQA_EUNSUPPORTED = -2, /* valid, but no kernel is built for it (e.g. d_h > 256) */
+    GQA_EWORKSPACE = -3,   /* decode workspace missing or too small */
+    GQA_EHIP = -4          /* the HIP runtime reported an error at launch */
+};
+
+/* Kernel selection for attn_prefill_ex (attn_prefill always uses GQA_ALGO_AUTO). */
+enum gqa_algo {
+    GQA_ALGO_AUTO = 0,    /* fastest kernel built for the shape */
+    GQA_ALGO_GENERIC = 1, /* vector-ALU kernel: any d_h in [1, 256], fp32 or bf16 */
+    GQA_ALGO_MFMA = 2     /* bf16 matrix-core kernel: d_h a multiple of 16, <= 128 */
+};
+
+/*
+ * Full-sequence prefill (Riftco "Dataflow and shapes": attention over [B, H, T, d_h];
+ * Hesper "Causal Masking" for the mask).
+ *
+ *   q, out : [B, Hq,  T, d_h]   (q of dtype; out float32)
+ *   k, v   : [B, Hkv, T, d_h]   (dtype)
+ *   scale  : multiplies q.k (1/sqrt(d_h) in the pages; any finite value accepted)
+ *   causal : 1 = key j visible to row i only when j <= i; 0 = every key visible
+ *
+ * Errors: GQA_EINVAL for B, T < 0; Hq, Hkv <= 0; Hq % Hkv != 0; d_h <= 0; non-finite
+ * scale; causal not 0/1; dtype unknown; a NULL or non-16-byte-aligned pointer when the
+ * tensor is non-empty.  GQA_EUNSUPPORTED for d_h > 256.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                 int T, int d_h, float scale, int causal, int dtype, void* stream);
+
+/* attn_prefill with an explicit kernel choice (enum gqa_algo).  GQA_ALGO_MFMA on a shape
+ * or dtype it does not cover returns GQA_EUNSUPPORTED, also when B or T is 0 (so an
+ * empty call with NULL pointers asks whether the kernel covers a shape). */
+int attn_prefill_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                    int Hkv, int T, int d_h, float scale, int causal, int dtype, int algo,
+                    void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_cached needs for this shape (0 when it needs
+ * none).  Pure host arithmetic; the same arguments always give the same answer.
+ * Returns 0 for arguments attn_decode_cached would reject.
+ */
+size_t attn_decode_workspace_bytes(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
+                                   int dtype);
+
+/* Number of key chunks the decode kernels split each sequence's history into for this
+ * shape (1 = no split).  Pure host arithmetic, for diagnostics and tests. */
+int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
+                           int dtype);
+
+/*
+ * Cached decode (makarna's CausalAttentionCached; the cache read of the multi-query
+ * primer's section 2.4 "Incremental: one token at a time").
+ *
+ *   q, out          : [B, newTokens, Hq, d_h]  new-token queries, token-major (q of dtype,
+ *                     out float32)
+ *   kcache, vcache  : [B, Hkv, totalLen, d_h]  full history per sequence, head-major (the
+ *                     Hesper KV cache layout), with the new tokens' K/V already written at
+ *                     positions startPos .. startPos+newTokens-1
+ *   startPos        : absolute position of the first new token; new token i attends to
+ *                     keys 0 .. startPos+i
+ *   scale           : fixed at 1/sqrt(d_h), as in CausalAttentionCached
+ *   workspace       : device buffer of at least attn_decode_workspace_bytes(...) bytes
+ *                     (may be NULL when that is 0); contents on entry are ignored
+ *
+ * Errors: GQA_EINVAL for B, newTokens, totalLen, startPos < 0; startPos+newTokens >
+ * totalLen; Hq, Hkv <= 0; Hq % Hkv != 0; d_h <= 0; dtype unknown; NULL or misaligned
+ * pointers for non-empty tensors.  GQA_EUNSUPPORTED for d_h > 256.  GQA_EWORKSPACE when
+ * workspace_bytes is below the required size or workspace is NULL while it is needed.
+ */
+int attn_decode_cached(const void* q, const void* kcache, const void* vcache, float* out,
+                       int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -103,7 +103,11 @@ static void run_unit(const job_t *J, int b, int h, double *row) {
         if (J->out) {
             double *o = J->out + (((size_t)b * J->Hq + h) * Tq + i) * (size_t)d;
             for (int e = 0; e < d; ++e) o[e] = 0.0;
+            /* the sum runs over allowed keys only: a masked key's value row is
+             * never read, so nothing after position p_i can reach row i (the
+             * makarna loop stops at maxKeyPos the same way) */
             for (int j = 0; j < Tk; ++j) {
+                if (J->causal && (long)j > p) continue;
                 const double pj = row[j];
                 const double *vj = vg + (size_t)j * d;
                 for (int e = 0; e < d; ++e) o[e] += pj * vj[e];

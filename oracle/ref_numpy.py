@@ -6,7 +6,8 @@ way the "Grouped-Query Attention" chapter's eager reference does it (section
 form the full score grid, add the causal -inf bias, softmax over keys, multiply
 by V.  Section 5.3 of that chapter checks one implementation against an
 independent second one; this module plays that role for the C oracle.
-Only meant for small shapes (it materializes [B, Hq, Tq, Tk]).
+Only meant for small shapes (it materializes [B, Hq, Tq, Tk]) and finite inputs
+(a non-finite future value would reach earlier rows through 0 * inf here).
 """
 from __future__ import annotations
 

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gqa_attn.h declares, and rejects bad arguments on the host before any
+launch (validation never touches the device, so these calls are safe without one).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+gqa = pytest.importorskip("grouped_query_attention_amd")
+lib = gqa.lib
+
+EINVAL, EUNSUP, EWS, OK = gqa.GQA_EINVAL, gqa.GQA_EUNSUPPORTED, gqa.GQA_EWORKSPACE, gqa.GQA_OK
+F32, BF16 = gqa.GQA_F32, gqa.GQA_BF16
+A16 = 0x10000  # a 16-byte-aligned non-null fake pointer; never dereferenced (validation fails first
+               # or the call has nothing to do)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert names, "no functions parsed from the header"
+    assert sorted(gqa.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror():
+    for code in (OK, EINVAL, EUNSUP, EWS, gqa.GQA_EHIP, 12345):
+        s = gqa.attn_strerror(code)
+        assert isinstance(s, str) and s
+
+
+def prefill(q=A16, k=A16, v=A16, out=A16, B=1, Hq=2, Hkv=1, T=4, d=8, scale=0.5, causal=1, dtype=BF16,
+            algo=0):
+    return lib.attn_prefill_ex(q, k, v, out, B, Hq, Hkv, T, d, ctypes.c_float(scale), causal, dtype, algo,
+                               None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=3, Hkv=2), EINVAL),            # Hq not a multiple of Hkv
+    (dict(Hkv=0), EINVAL),
+    (dict(Hq=0), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(T=-1), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(d=257), EUNSUP),                  # no kernel beyond 256
+    (dict(scale=float("inf")), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(causal=2), EINVAL),
+    (dict(dtype=7), EINVAL),
+    (dict(algo=9), EINVAL),
+    (dict(q=None), EINVAL),                 # null pointer for a non-empty tensor
+    (dict(out=A16 + 4), EINVAL),            # misaligned
+    (dict(d=8, algo=2, dtype=F32), EUNSUP),  # matrix-core kernel is bf16 only
+    (dict(d=8, algo=2), EUNSUP),            # d not a multiple of 16
+])
+def test_prefill_rejects(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_empty_is_noop():
+    # nothing to compute: returns OK without touching the (null) pointers
+    assert prefill(q=None, k=None, v=None, out=None, B=0) == OK
+    assert prefill(q=None, k=None, v=None, out=None, T=0) == OK
+
+
+def decode(q=A16, kc=A16, vc=A16, out=A16, n=1, L=16, sp=15, Hq=4, Hkv=1, d=64, B=1, dtype=BF16, ws=A16,
+           ws_bytes=1 << 30):
+    return lib.attn_decode_cached(q, kc, vc, out, n, L, sp, Hq, Hkv, d, B, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sp=16), EINVAL),         # startPos + newTokens > totalLen
+    (dict(n=2, sp=15), EINVAL),
+    (dict(sp=-1), EINVAL),
+    (dict(n=-1), EINVAL),
+    (dict(L=-1), EINVAL),
+    (dict(Hq=6, Hkv=4), EINVAL),
+    (dict(Hkv=0), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(d=300), EUNSUP),
+    (dict(dtype=3), EINVAL),
+    (dict(kc=None), EINVAL),
+    (dict(vc=A16 + 2), EINVAL),
+])
+def test_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_empty_is_noop():
+    assert decode(q=None, kc=None, vc=None, out=None, n=0, sp=16) == OK
+    assert decode(q=None, kc=None, vc=None, out=None, B=0) == OK
+
+
+def test_decode_workspace_checked_before_launch():
+    B, n, L, Hq, Hkv, d = 64, 4, 32768, 32, 8, 128
+    need = gqa.attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d, BF16)
+    if need == 0:
+        pytest.skip("this shape needs no workspace")
+    args = dict(n=n, L=L, sp=L - n, Hq=Hq, Hkv=Hkv, d=d, B=B)
+    assert decode(ws=None, ws_bytes=need, **args) == EWS
+    assert decode(ws=A16, ws_bytes=need - 1, **args) == EWS
+    assert decode(ws=A16 + 8, ws_bytes=need, **args) == EINVAL
+
+
+def test_decode_plan_host_logic():
+    """The split plan is a pure function of the shape: deterministic, at least one
+    chunk, and the workspace covers one (max, sum, numerator) partial per chunk,
+    query row and head dim when the history is split."""
+    for (B, n, L, Hq, Hkv, d) in [(64, 1, 32768, 32, 8, 128), (64, 4, 32768, 32, 8, 128),
+                                  (1, 1, 17, 4, 1, 64), (2, 3, 1000, 8, 2, 128), (1, 1, 1, 1, 1, 16)]:
+        s1 = gqa.attn_decode_num_splits(B, n, L, Hq, Hkv, d, BF16)
+        s2 = gqa.attn_decode_num_splits(B, n, L, Hq, Hkv, d, BF16)
+        w = gqa.attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d, BF16)
+        assert s1 == s2 >= 1
+        assert s1 <= L
+        if s1 > 1:
+            assert w >= s1 * B * n * Hq * (d + 2) * 4
+        assert w == gqa.attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d, BF16)
+    # invalid shapes plan nothing
+    assert gqa.attn_decode_num_splits(1, 2, 1, 4, 1, 64, BF16) == 0
+    assert gqa.attn_decode_workspace_bytes(1, 1, 8, 3, 2, 64, BF16) == 0

@@ -438,3 +438,15 @@ def test_pins_catch_planted_mistakes(kind):
         if r is not None:
             failures.append(pin.__name__)
     assert failures, "planted mistake %r passed every pin" % kind
+
+
+def test_c_oracle_never_reads_masked_values():
+    """Future value rows are not part of row i's sum at all (not even as 0 * v):
+    a NaN planted after position t leaves every row before t finite."""
+    rng = np.random.default_rng(13)
+    q, k, v = rand(rng, 1, 2, 9, 4), rand(rng, 1, 1, 9, 4), rand(rng, 1, 1, 9, 4)
+    v[0, 0, 5, 1] = np.nan
+    k[0, 0, 6, 2] = np.nan
+    o = oracle.attention(q, k, v, 0.5, True, 0)
+    assert np.isfinite(o[0, :, :5]).all()
+    assert np.isnan(o[0, :, 5:]).any(-1).all()
