@@ -36,13 +36,14 @@ namespace gqa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 128;        // query rows per head per workgroup
+constexpr int kWgWaves = 8;     // waves per workgroup (HPW heads x kWgWaves/HPW row slices)
 constexpr int kBN = 64;         // keys per LDS tile
 constexpr float kLazyTau = 8.f; // log2 growth of the row max tolerated before rescaling
 
@@ -50,14 +51,18 @@ template <int D>
 struct Geo {
   static constexpr int kSteps = D / 16;           // K-steps of the S^T contraction
   static constexpr int kDBlocks = (D + 31) / 32;  // 32-row blocks of O^T
-  // K rows: an odd number of 16-byte chunks apart, so 8 lanes reading the same
-  // column of 8 consecutive rows hit 8 different bank groups.
+  // K rows: an odd number of 16-byte chunks apart, so the 16 lanes served per bank
+  // cycle (same column, 16 consecutive rows) hit 16 different 16-byte bank groups.
   static constexpr int kKStride = 2 * D + 16;
-  // V rows: the transposed read touches 4 rows x 32 bytes per 16 lanes; a stride of
-  // 32 or 96 mod 128 bytes puts those 4 rows in distinct banks.  Rows are read up to
-  // the next multiple of 32 head dims (the padding feeds discarded O^T rows only).
+  // V rows: per bank cycle (64 banks x 4 bytes) the transposed reads of 32 lanes touch
+  // 4 consecutive rows x 64 bytes; a row stride of 64 or 192 mod 256 bytes puts those
+  // 4 rows in distinct banks (measured conflict-free; 32 mod 128 is not).  Rows are
+  // read up to the next multiple of 32 head dims (the padding feeds discarded O^T rows
+  // only).
   static constexpr int kVRead = 64 * kDBlocks;
-  static constexpr int kVStride = kVRead + 32;
+  static constexpr int kVStride = (kVRead % 256 <= 64) ? kVRead - kVRead % 256 + 64
+                                  : (kVRead % 256 <= 192) ? kVRead - kVRead % 256 + 192
+                                                          : kVRead - kVRead % 256 + 320;
   static constexpr int kKTile = kBN * kKStride;
   static constexpr int kVTile = kBN * kVStride;
   static constexpr int kLds = 2 * (kKTile + kVTile);  // double-buffered
@@ -66,7 +71,7 @@ struct Geo {
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
@@ -75,12 +80,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D, int HPW>
-__global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
+__global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int Hq, int Hkv, int T, float c,
     unsigned qsign, int causal, int n_qtiles, int n_hgroups, int B) {
   using G_ = Geo<D>;
-  constexpr int NT = HPW * 256;
+  constexpr int NT = kWgWaves * 64;
+  constexpr int SLICES = kWgWaves / HPW;  // 32-row slices per head
+  constexpr int QT = 32 * SLICES;         // query rows per head per workgroup
   constexpr int NCH = (G_::kChunks + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) char smem[G_::kLds];
 
@@ -97,10 +104,10 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
   const int rem = bid % per_qt;
   const int hg = rem % n_hgroups;
   const int b = rem / n_hgroups;
-  const int h = hg * HPW + wave / 4;
+  const int h = hg * HPW + wave / SLICES;
   const int g = (hg * HPW) / (Hq / Hkv);
-  const int q0 = qt * kBM;
-  const int qw = q0 + (wave & 3) * 32;   // first query row of this wave
+  const int q0 = qt * QT;
+  const int qw = q0 + (wave % SLICES) * 32;   // first query row of this wave
   const int qi = qw + col;               // this lane's query row (absolute position)
 
   const long long kv_base = ((long long)b * Hkv + g) * (long long)T * D;
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
   float m_run = -INFINITY;  // running max, log2 units (same in both lane halves)
   float l_part = 0.f;       // this lane's share of the normalizer
 
-  const int kend = causal ? min(T, q0 + kBM) : T;
+  const int kend = causal ? min(T, q0 + QT) : T;
   const int ntiles = (kend + kBN - 1) / kBN;
 
   // cooperative tile load: global -> registers -> LDS
@@ -135,15 +142,13 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = tid + i * NT;
-      kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = u32x4{0u, 0u, 0u, 0u};
       if (ch < G_::kChunks) {
+        // rows at or past T load row T-1 instead: those keys are masked, and their
+        // (finite) values meet probability 0
         const int row = ch / (D / 8), c16 = ch % (D / 8);
-        const int key = t * kBN + row;
-        if (key < T) {
-          kreg[i] = *reinterpret_cast<const u32x4*>(kg + (long long)key * D + c16 * 8);
-          vreg[i] = *reinterpret_cast<const u32x4*>(vg + (long long)key * D + c16 * 8);
-        }
+        const long long off = (long long)min(t * kBN + row, T - 1) * D + c16 * 8;
+        kreg[i] = *reinterpret_cast<const u32x4*>(kg + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vg + off);
       }
     }
   };
@@ -175,22 +180,54 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
     if (active) {
       const char* kl = smem + buf * G_::kKTile;
       const char* vl = smem + 2 * G_::kKTile + buf * G_::kVTile;
-      // second 32-key half entirely above the diagonal?
-      const int nsb = (causal && k0 + 32 > qw + 31) ? 1 : 2;
       const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
 
+      // S^T = K Q^T: all K fragments of the tile are read before the matrix ops so
+      // the LDS latency is paid once, and the two 32-key blocks form two
+      // independent accumulation chains.
       f32x16 s[2];
+      {
+        bf16x8 kf[2][G_::kSteps];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        s[sb] = f32x16{};
-        if (sb < nsb) {
+        for (int sb = 0; sb < 2; ++sb) {
           const char* krow = kl + (sb * 32 + col) * G_::kKStride + half * 16;
 #pragma unroll
-          for (int st = 0; st < G_::kSteps; ++st) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + st * 32);
-            s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[sb], 0, 0, 0);
-          }
+          for (int st = 0; st < G_::kSteps; ++st)
+            kf[sb][st] = *reinterpret_cast<const bf16x8*>(krow + st * 32);
         }
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < G_::kSteps; ++st) {
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][st], qf[st], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][st], qf[st], s[1], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+
+      // V^T fragments for O^T += V^T P^T, issued now so their latency hides under the
+      // softmax.  Transposed-read addressing inside each 16-lane group: lane s reads 4
+      // head dims (m0 + 4*(s%4) ..) of key row (k0p + s/4); after the transpose lane s
+      // holds head dim m0 + s of keys k0p .. k0p+3.
+      bf16x8 vf[2][2][G_::kDBlocks];
+      {
+        const int grp = lane >> 4, sl = lane & 15;
+        const int voff = (sl >> 2) * G_::kVStride + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const char* vrow = vl + (32 * sb + 16 * kk + 4 * half) * G_::kVStride + voff;
+#pragma unroll
+            for (int db = 0; db < G_::kDBlocks; ++db) {
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + db * 64));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(vrow + 8 * G_::kVStride + db * 64));
+              vf[sb][kk][db] = __builtin_bit_cast(
+                  bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+          }
       }
 
       // mask (diagonal tiles only): key j of accumulator r is
@@ -202,20 +239,16 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
           for (int r = 0; r < 16; ++r) {
             const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
             const bool ok = causal ? (j <= qi) : (j < T);
-            if (!ok || sb >= nsb) s[sb][r] = -INFINITY;
+            if (!ok) s[sb][r] = -INFINITY;
           }
-      } else if (nsb == 1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[1][r] = -INFINITY;
       }
 
-      float mx = s[0][0];
+      // NaN-propagating maximum lowers to v_maximum3_f32 with no operand
+      // canonicalization (fmaxf would add one v_max per score)
+      float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-      if (nsb == 2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      }
+      for (int r = 1; r < 16; ++r)
+        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[0][r]), s[1][r]);
       mx = pair_max(mx);
       const float mt = mx * c;  // tile max in log2 units
       const bool need = mt > m_run + kLazyTau;
@@ -228,46 +261,35 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
         m_run = m_new;
       }
 
+      // p = 2^(s*c - m), rounded to bf16 for the P V product; the normalizer sums the
+      // same bf16 values, two per v_dot2_f32_bf16 against (1, 1)
       bf16x8 pb[2][2];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float lsum[2] = {0.f, 0.f};
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (sb >= nsb) break;
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m_run));
-          s[sb][r] = p;
-          l_part += p;
-        }
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+          for (int e = 0; e < 8; ++e)
+            pb[sb][kk][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][8 * kk + e], c, -m_run));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pb[sb][kk][e] = (__bf16)s[sb][8 * kk + e];
-      }
-
-      // O^T += V^T P^T.  Transposed-read addressing inside each 16-lane group:
-      // lane s reads 4 head dims (m0 + 4*(s%4) ..) of key row (k0p + s/4); after the
-      // transpose lane s holds head dim m0 + s of keys k0p .. k0p+3.
-      const int grp = lane >> 4, sl = lane & 15;
-      const int m0 = 16 * (grp & 1);
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (sb < nsb) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int k0p = 32 * sb + 16 * kk + 4 * half;
-            const char* vrow = vl + (k0p + (sl >> 2)) * G_::kVStride + (m0 + 4 * (sl & 3)) * 2;
-#pragma unroll
-            for (int db = 0; db < G_::kDBlocks; ++db) {
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + db * 64));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_i16x4*)(vrow + 8 * G_::kVStride + db * 64));
-              const bf16x8 a = __builtin_bit_cast(
-                  bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[sb][kk], o[db], 0, 0, 0);
-            }
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[sb][kk][e], pb[sb][kk][e + 1]};
+            lsum[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[kk], false);
           }
         }
-      }
+      l_part += lsum[0] + lsum[1];
+
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int db = 0; db < G_::kDBlocks; ++db)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][kk][db], pb[sb][kk], o[db], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
 
     if (t + 1 < ntiles) lstore(buf ^ 1);
@@ -295,7 +317,8 @@ __global__ __launch_bounds__(HPW * 256, 2) void prefill_mfma_kernel(
 
 template <int D, int HPW>
 hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
-  const int n_qtiles = (a.T + kBM - 1) / kBM;
+  constexpr int QT = 32 * (kWgWaves / HPW);
+  const int n_qtiles = (a.T + QT - 1) / QT;
   const int n_hgroups = a.Hq / HPW;
   const long long nblocks = (long long)n_qtiles * n_hgroups * a.B;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -304,7 +327,7 @@ hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   // masked scores at -inf without changing any visible weight measurably
   if (c == 0.f) c = 1e-30f;
   const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW>), dim3((unsigned)nblocks), dim3(HPW * 256), 0,
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW>), dim3((unsigned)nblocks), dim3(kWgWaves * 64), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, a.Hq, a.Hkv, a.T, c, qsign, a.causal,
                      n_qtiles, n_hgroups, a.B);
