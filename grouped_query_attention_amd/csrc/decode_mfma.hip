@@ -1,16 +1,362 @@
-// decode_mfma.hip -- split-KV cached decode (placeholder until the kernel lands).
+// decode_mfma.hip -- split-KV cached GQA decode for gfx950 (bf16 cache, fp32 out).
+//
+// The new tokens at positions startPos .. startPos+n-1 attend to every cached key up
+// to their own position (makarna's CausalAttentionCached key limit startPos+qi+1).
+// Every call reads the whole visible cache once -- the cost the multi-query primer's
+// section 2.4 "Incremental: one token at a time" points at -- so the kernel is built
+// to stream K and V at HBM rate:
+//
+//  * Work item = one wave = (sequence b, K/V head g, key chunk).  The G*n query rows of
+//    the group (G query heads x n tokens) are the columns of one 16-wide MFMA tile, so
+//    every K/V byte is read once per group, not once per query head.
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the A operand (16 keys x 32 head
+//    dims) is loaded straight from HBM -- each load instruction reads 16 key rows x
+//    64 contiguous bytes -- and Q^T stays in registers.
+//  * O^T = V^T P^T needs V with keys along the contraction; the 32-key V tile goes
+//    through a wave-private LDS tile and ds_read_b64_tr_b16.  The S^T accumulator,
+//    converted to bf16, is the P^T operand directly (keys in the order
+//    {4g..4g+3, 16+4g..16+4g+3} for lane group g; V^T uses the same order).
+//  * The next tile's K and V are in flight while the current one is computed.
+//  * Online softmax in log2 units with a lazily moved running max.  Each chunk leaves
+//    a partial (m, l, O) in the workspace; decode_merge_kernel combines them:
+//    M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+//    The merge is exact in exact arithmetic; it is the per-row statistics of Riftco's
+//    "Two exact full-sequence algorithms" applied across key chunks.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include "launch.h"
 
 namespace gqa {
+namespace {
 
-DecodePlan plan_decode(int, int, int total_len, int, int, int, int) {
-  return DecodePlan{1, total_len, 0, false};
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWaves = 4;        // independent waves per workgroup
+constexpr int kTile = 32;        // keys per tile
+constexpr int kCols = 16;        // query columns per MFMA tile
+constexpr float kLazyTau = 8.f;  // log2 growth of the running max tolerated before rescale
+constexpr int kTargetWaves = 8192;
+
+template <int D>
+struct DGeo {
+  static constexpr int kSteps = (D + 31) / 32;  // 32-wide K-steps of S^T (last may be padded)
+  static constexpr int kDBlocks = D / 16;       // 16-row blocks of O^T
+  static constexpr int kChunks = kTile * D / 8;  // 16-byte chunks of a V tile
+  static constexpr int kPerLane = kChunks / 64;  // V chunks staged per lane
+  // Transposed reads of the 4 lane groups touch 16 consecutive rows x 32 bytes; an odd
+  // multiple of 32 bytes as row stride spreads each half-wave over 8 distinct 32-byte
+  // bank slots.
+  static constexpr int kVStride = ((2 * D / 32) % 2 == 1) ? 2 * D : 2 * D + 32;
+  static constexpr int kLdsPerWave = kTile * kVStride;
+};
+
+__device__ __forceinline__ float xmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// reduce over the 4 lane groups (lanes l, l^16, l^32, l^48 hold the same query column)
+__device__ __forceinline__ float group_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = xmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return xmax(x, __shfl_xor(x, 16));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return x + __shfl_xor(x, 16);
 }
 
-hipError_t launch_attn_decode_mfma(const DecodeArgs&, const DecodePlan&, hipStream_t) {
-  return hipErrorInvalidValue;
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, float* __restrict__ opart, float* __restrict__ mlpart, int n,
+    int Hq, int Hkv, int L, int start_pos, float c, int nsplit, int chunk, int ncb,
+    int total_waves) {
+  using G_ = DGeo<D>;
+  __shared__ __attribute__((aligned(16))) char smem[kWaves * G_::kLdsPerWave];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int gw = blockIdx.x * kWaves + wave;
+  if (gw >= total_waves) return;  // whole wave; no workgroup barrier is used
+  const int split = gw % nsplit;
+  const int unit = gw / nsplit;
+  const int cb = unit % ncb;
+  const int bg = unit / ncb;
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+  const int G = Hq / Hkv;
+  const int ncols = G * n;
+  const int kv_len = start_pos + n;  // keys any new token can see
+  const int c0 = split * chunk;
+  if (c0 >= kv_len) return;  // empty chunk: the merge only reads chunks below kv_len
+  const int c1 = min(c0 + chunk, kv_len);
+
+  const int col = lane & 15;  // query column of the lane
+  const int grp = lane >> 4;  // lane group: keys 4*grp.. of each 16-key block
+  const int cidx = cb * kCols + col;
+  const bool col_ok = cidx < ncols;
+  const int tok = col_ok ? cidx / G : 0;  // columns are token-major: (token, head in group)
+  const int hq = g * G + (col_ok ? cidx % G : 0);
+  const int qpos = start_pos + tok;  // absolute position of the column's token
+
+  // Q^T fragments: column cidx, head dims 32*st + 8*grp + 0..7 (zero past D)
+  bf16x8 qf[G_::kSteps];
+#pragma unroll
+  for (int st = 0; st < G_::kSteps; ++st) {
+    const int d0 = 32 * st + 8 * grp;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (col_ok && d0 < D)
+      x = *reinterpret_cast<const u32x4*>(q + (((long long)b * n + tok) * Hq + hq) * D + d0);
+    qf[st] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  const long long kv_base = ((long long)b * Hkv + g) * (long long)L * D;
+  const uint16_t* kg = kc + kv_base;
+  const uint16_t* vg = vc + kv_base;
+  char* vl = smem + wave * G_::kLdsPerWave;
+
+  // K fragments of a tile (A operand): block kb, step st -> key j0 + 16kb + col,
+  // head dims 32st + 8grp .. +7.  Keys past the cache end are clamped (masked anyway).
+  auto load_k = [&](int j0, bf16x8 (&kf)[2][G_::kSteps]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const long long row = (long long)min(j0 + 16 * kb + col, L - 1) * D;
+#pragma unroll
+      for (int st = 0; st < G_::kSteps; ++st) {
+        const int d0 = 32 * st + 8 * grp;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (d0 < D) x = *reinterpret_cast<const u32x4*>(kg + row + d0);
+        kf[kb][st] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  };
+  // V tile rows j0..j0+31, contiguous 16-byte chunks per lane (4 rows per 1 KB load)
+  auto load_v = [&](int j0, u32x4 (&vr)[G_::kPerLane]) {
+#pragma unroll
+    for (int i = 0; i < G_::kPerLane; ++i) {
+      const int ch = lane + 64 * i;
+      const int r = ch / (D / 8), cc = ch % (D / 8);
+      vr[i] = *reinterpret_cast<const u32x4*>(vg + (long long)min(j0 + r, L - 1) * D + cc * 8);
+    }
+  };
+  auto store_v = [&](const u32x4 (&vr)[G_::kPerLane]) {
+#pragma unroll
+    for (int i = 0; i < G_::kPerLane; ++i) {
+      const int ch = lane + 64 * i;
+      const int r = ch / (D / 8), cc = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(vl + r * G_::kVStride + cc * 16) = vr[i];
+    }
+  };
+
+  f32x4 o[G_::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < G_::kDBlocks; ++db) o[db] = f32x4{};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // transposed-read addressing: lane s of group grp reads 4 head dims (16db + 4(s%4) ..)
+  // of key row k0 + s/4; after the transpose it holds head dim 16db + s of keys k0..k0+3
+  const int sl = lane & 15;
+  const int voff = (sl >> 2) * G_::kVStride + 4 * (sl & 3) * 2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  bf16x8 kf[2][G_::kSteps];
+  u32x4 vr[G_::kPerLane];
+  load_k(c0, kf);
+  load_v(c0, vr);
+  for (int j0 = c0; j0 < c1; j0 += kTile) {
+    store_v(vr);  // this wave's earlier reads of the tile buffer are complete
+    bf16x8 kn[2][G_::kSteps];
+    const bool more = j0 + kTile < c1;
+    if (more) {
+      load_k(j0 + kTile, kn);
+      load_v(j0 + kTile, vr);
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{};
+#pragma unroll
+      for (int st = 0; st < G_::kSteps; ++st)
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][st], qf[st], s[kb], 0, 0, 0);
+    }
+    // keys past the chunk, or after the column's own position, get no weight
+    if (j0 + kTile > c1 || j0 + kTile - 1 > start_pos) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + 16 * kb + 4 * grp + r;
+          if (j >= c1 || j > qpos) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = xmax(xmax(xmax(s[0][0], s[0][1]), xmax(s[0][2], s[0][3])),
+                    xmax(xmax(s[1][0], s[1][1]), xmax(s[1][2], s[1][3])));
+    mx = group_max(mx);
+    const float mt = mx * c;
+    const bool need = mt > m_run + kLazyTau;
+    if (__any(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < G_::kDBlocks; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    // a column whose keys so far are all masked keeps m = -inf: use 0 as reference
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pb;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        pb[4 * kb + r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_ref));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pr = {pb[e], pb[e + 1]};
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_part, false);
+    }
+
+    // O^T += V^T P^T over the tile's 32 keys (one K-step)
+    const char* v0 = vl + (4 * grp) * G_::kVStride + voff;
+#pragma unroll
+    for (int db = 0; db < G_::kDBlocks; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + db * 32));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 16 * G_::kVStride + db * 32));
+      const bf16x8 a =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
+    }
+    if (more) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < G_::kSteps; ++st) kf[kb][st] = kn[kb][st];
+    }
+  }
+
+  // partial (m, l, O) of this chunk for every valid column.  O^T row (head dim) of
+  // accumulator r in block db is 16db + 4grp + r.
+  const float l_tot = group_sum(l_part);
+  if (col_ok) {
+    const long long pidx = ((long long)(b * Hkv + g) * nsplit + split) * ncols + cidx;
+    float* op = opart + pidx * D;
+#pragma unroll
+    for (int db = 0; db < G_::kDBlocks; ++db)
+      *reinterpret_cast<f32x4*>(op + 16 * db + 4 * grp) = o[db];
+    if (grp == 0) {
+      mlpart[2 * pidx] = m_run;
+      mlpart[2 * pidx + 1] = l_tot;
+    }
+  }
+}
+
+// One 64-thread block per output row (b, g, column): combine the chunk partials.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ opart,
+                                                          const float* __restrict__ mlpart,
+                                                          float* __restrict__ out, int n, int Hq,
+                                                          int Hkv, int nsplit, int nvalid) {
+  constexpr int PER = (D + 63) / 64;
+  const int G = Hq / Hkv;
+  const int ncols = G * n;
+  const int row = blockIdx.x;  // (b * Hkv + g) * ncols + cidx
+  const int cidx = row % ncols;
+  const int bg = row / ncols;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int tok = cidx / G, hq = g * G + cidx % G;
+  const long long base = (long long)bg * nsplit * ncols + cidx;  // partial index of split 0
+
+  float M = -INFINITY;
+  for (int s = 0; s < nvalid; ++s) M = xmax(M, mlpart[2 * (base + (long long)s * ncols)]);
+  float Lsum = 0.f, acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int s = 0; s < nvalid; ++s) {
+    const long long p = base + (long long)s * ncols;
+    const float w = __builtin_amdgcn_exp2f(mlpart[2 * p] - M);  // 0 for an all-masked chunk
+    Lsum += mlpart[2 * p + 1] * w;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = threadIdx.x + 64 * e;
+      if (d < D) acc[e] += opart[p * D + d] * w;
+    }
+  }
+  const float inv = 1.f / Lsum;
+  float* orow = out + (((long long)b * n + tok) * Hq + hq) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = threadIdx.x + 64 * e;
+    if (d < D) orow[d] = acc[e] * inv;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const int ncols = G * a.n;
+  const int ncb = (ncols + kCols - 1) / kCols;
+  const long long total = (long long)a.B * a.Hkv * ncb * p.nsplit;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long np = (long long)a.B * a.Hkv * p.nsplit * ncols;
+  float* opart = static_cast<float*>(a.workspace);
+  float* mlpart = opart + np * D;
+  const float c = a.scale * 1.4426950408889634f;
+  const int blocks = (int)((total + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(blocks), dim3(kWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
+                     static_cast<const uint16_t*>(a.vc), opart, mlpart, a.n, a.Hq, a.Hkv, a.L,
+                     a.start_pos, c, p.nsplit, p.chunk, ncb, (int)total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int kv_len = a.start_pos + a.n;
+  const int nvalid = (kv_len + p.chunk - 1) / p.chunk;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * ncols), dim3(64), 0, stream,
+                     opart, mlpart, a.out, a.n, a.Hq, a.Hkv, p.nsplit, nvalid);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Pure function of the shape: enough chunks that the launch has ~kTargetWaves waves,
+// each chunk a multiple of the 32-key tile; partials are (d + 2) floats per chunk,
+// query row and head.
+DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int dtype) {
+  DecodePlan p{1, total_len, 0, false};
+  p.mfma = dtype == kBF16 && d % 16 == 0 && d <= 128 && total_len > 0;
+  if (!p.mfma) return p;
+  const int ncols = (Hq / Hkv) * n;
+  const long long units = (long long)B * Hkv * ((ncols + kCols - 1) / kCols);
+  long long want = (kTargetWaves + units - 1) / units;
+  const long long max_split = (total_len + kTile - 1) / kTile;
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  long long chunk = (total_len + want - 1) / want;
+  chunk = (chunk + kTile - 1) / kTile * kTile;
+  p.chunk = (int)chunk;
+  p.nsplit = (int)((total_len + chunk - 1) / chunk);
+  p.workspace = (size_t)B * Hq * n * (size_t)p.nsplit * (size_t)(d + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  switch (a.d) {
+    case 16: return launch_d<16>(a, p, stream);
+    case 32: return launch_d<32>(a, p, stream);
+    case 48: return launch_d<48>(a, p, stream);
+    case 64: return launch_d<64>(a, p, stream);
+    case 80: return launch_d<80>(a, p, stream);
+    case 96: return launch_d<96>(a, p, stream);
+    case 112: return launch_d<112>(a, p, stream);
+    case 128: return launch_d<128>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gqa
