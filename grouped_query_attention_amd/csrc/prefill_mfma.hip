@@ -254,7 +254,9 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       const bool need = mt > m_run + kLazyTau;
       if (__any(need)) {
         const float m_new = need ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // lanes that keep their max keep their scale: exp2(m - m) would be NaN
+        // for a column that has seen only masked keys (m = -inf)
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         l_part *= alpha;
 #pragma unroll
         for (int db = 0; db < G_::kDBlocks; ++db) o[db] *= alpha;

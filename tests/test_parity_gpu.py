@@ -118,6 +118,10 @@ DECODE = [
     (1, 2, 4, 4, 4099, 80),
     (2, 1, 16, 1, 2049, 128),
     (1, 5, 2, 1, 77, 24),
+    (1, 4, 16, 2, 300, 128),   # 32 query columns per group: two MFMA column blocks
+    (2, 5, 16, 4, 2000, 64),   # 20 columns per group, a ragged second block
+    (1, 40, 2, 1, 100, 64),    # new tokens span several 32-key chunks: all-masked partials
+    (1, 33, 4, 1, 65, 128),    # every key is new; chunks smaller than the token span
 ]
 
 
