@@ -65,8 +65,7 @@ struct Geo {
                                                           : kVRead - kVRead % 256 + 320;
   static constexpr int kKTile = kBN * kKStride;
   static constexpr int kVTile = kBN * kVStride;
-  static constexpr int kLds = 2 * (kKTile + kVTile);  // double-buffered
-  static constexpr int kChunks = kBN * D / 8;          // 16-byte chunks per tile
+  static constexpr int kBuf = kKTile + kVTile;  // one stage: K tile then V tile
 };
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -88,8 +87,12 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   constexpr int NT = kWgWaves * 64;
   constexpr int SLICES = kWgWaves / HPW;  // 32-row slices per head
   constexpr int QT = 32 * SLICES;         // query rows per head per workgroup
-  constexpr int NCH = (G_::kChunks + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) char smem[G_::kLds];
+  // Two stages in two separate LDS arrays: the loop is unrolled by two so each
+  // iteration reads one array while direct global->LDS loads fill the other, and the
+  // compiler can see they do not alias (one shared array indexed by the stage makes it
+  // wait for the in-flight loads before every LDS read).
+  __shared__ __attribute__((aligned(16))) char lds_a[G_::kBuf];
+  __shared__ __attribute__((aligned(16))) char lds_b[G_::kBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,56 +139,74 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   const int kend = causal ? min(T, q0 + QT) : T;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  // cooperative tile load: global -> registers -> LDS
-  u32x4 kreg[NCH], vreg[NCH];
-  auto gload = [&](int t) {
+  // Tile staging with direct global->LDS loads (global_load_lds_dwordx4, no register
+  // staging): one wave instruction writes 64 consecutive 16-byte LDS slots; slot p of a
+  // tile is row p / P, chunk p % P of a row padded to P chunks.  A lane's source offset
+  // inside a tile is the same for every tile, so it is computed once here.  Padding
+  // slots re-read chunk 0 of their row.  In a ragged last tile, rows at or past T read
+  // row T-1 instead: those keys are masked, and their finite values meet probability 0.
+  constexpr int KP = G_::kKStride / 16, VP = G_::kVStride / 16, C16 = D / 8;
+  constexpr int KI = (KP + kWgWaves - 1) / kWgWaves;  // wave instructions per wave per tile
+  constexpr int VI = (VP + kWgWaves - 1) / kWgWaves;
+  int krow[KI], koff[KI], vrow[VI], voff[VI];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + i * NT;
-      if (ch < G_::kChunks) {
-        // rows at or past T load row T-1 instead: those keys are masked, and their
-        // (finite) values meet probability 0
-        const int row = ch / (D / 8), c16 = ch % (D / 8);
-        const long long off = (long long)min(t * kBN + row, T - 1) * D + c16 * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(kg + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vg + off);
+  for (int i = 0; i < KI; ++i) {
+    const int p = (wave + kWgWaves * i) * 64 + lane, r = p / KP, cc = p % KP;
+    krow[i] = r;
+    koff[i] = (cc < C16 ? cc : 0) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int p = (wave + kWgWaves * i) * 64 + lane, r = p / VP, cc = p % VP;
+    vrow[i] = r;
+    voff[i] = (cc < C16 ? cc : 0) * 16;
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto stage = [&](int t, char* dst) {
+    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kBN * D * 2;
+    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kBN * D * 2;
+    const bool ragged = t * kBN + kBN > T;
+    const int rmax = T - 1 - t * kBN;  // last valid row of this tile
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int inst = wave_u + kWgWaves * i;
+      if (inst < KP) {
+        const int r = ragged ? min(krow[i], rmax) : krow[i];
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(kb + r * (D * 2) + koff[i]),
+            (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int inst = wave_u + kWgWaves * i;
+      if (inst < VP) {
+        const int r = ragged ? min(vrow[i], rmax) : vrow[i];
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(vb + r * (D * 2) + voff[i]),
+            (__attribute__((address_space(3))) void*)(dst + G_::kKTile + inst * 1024), 16, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
-    char* kl = smem + buf * G_::kKTile;
-    char* vl = smem + 2 * G_::kKTile + buf * G_::kVTile;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + i * NT;
-      if (ch < G_::kChunks) {
-        const int row = ch / (D / 8), c16 = ch % (D / 8);
-        *reinterpret_cast<u32x4*>(kl + row * G_::kKStride + c16 * 16) = kreg[i];
-        *reinterpret_cast<u32x4*>(vl + row * G_::kVStride + c16 * 16) = vreg[i];
-      }
-    }
-  };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-
+  // One tile in two parts around the staging of the next tile.  The transposed V reads
+  // must not meet direct-to-LDS loads in flight (the compiler cannot tell them apart
+  // and would wait for the loads there), so the next tile's loads are issued after
+  // this tile's LDS reads, behind a compiler memory barrier, and overlap the softmax
+  // and the P V products.
+  auto step = [&](int t, const char* cur, char* nxt) {
     const int k0 = t * kBN;
     // keys k0.. are all beyond this wave's last row: nothing to do (causal)
     const bool active = !causal || k0 <= qw + 31;
+    const char* kl = cur;
+    const char* vl = cur + G_::kKTile;
+    const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
+    f32x16 s[2];
+    bf16x8 vf[2][2][G_::kDBlocks];
     if (active) {
-      const char* kl = smem + buf * G_::kKTile;
-      const char* vl = smem + 2 * G_::kKTile + buf * G_::kVTile;
-      const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
-
       // S^T = K Q^T: all K fragments of the tile are read before the matrix ops so
       // the LDS latency is paid once, and the two 32-key blocks form two
       // independent accumulation chains.
-      f32x16 s[2];
       {
         bf16x8 kf[2][G_::kSteps];
 #pragma unroll
@@ -210,7 +231,6 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       // softmax.  Transposed-read addressing inside each 16-lane group: lane s reads 4
       // head dims (m0 + 4*(s%4) ..) of key row (k0p + s/4); after the transpose lane s
       // holds head dim m0 + s of keys k0p .. k0p+3.
-      bf16x8 vf[2][2][G_::kDBlocks];
       {
         const int grp = lane >> 4, sl = lane & 15;
         const int voff = (sl >> 2) * G_::kVStride + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
@@ -230,6 +250,10 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
           }
       }
 
+    }
+    asm volatile("" ::: "memory");
+    if (t + 1 < ntiles) stage(t + 1, nxt);  // that array was freed by the last barrier
+    if (active) {
       // mask (diagonal tiles only): key j of accumulator r is
       // k0 + 32*sb + 8*(r/4) + 4*half + r%4
       if (diag) {
@@ -293,9 +317,16 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][kk][db], pb[sb][kk], o[db], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
     }
-
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
     __syncthreads();
+  };
+
+  stage(0, lds_a);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, lds_a, lds_b);
+    if (t + 1 < ntiles) step(t + 1, lds_b, lds_a);
   }
 
   // epilogue: O^T row (head dim) of accumulator r in block db is
