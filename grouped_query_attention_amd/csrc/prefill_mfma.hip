@@ -44,7 +44,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWgWaves = 8;     // waves per workgroup (HPW heads x kWgWaves/HPW row slices)
-constexpr int kBN = 64;         // keys per LDS tile
+constexpr int kBN = 64;         // keys per compute tile
+constexpr int kSub = 2;         // compute tiles per LDS stage (one barrier per stage)
+constexpr int kStage = kSub * kBN;
 constexpr float kLazyTau = 8.f; // log2 growth of the row max tolerated before rescaling
 
 template <int D>
@@ -63,8 +65,8 @@ struct Geo {
   static constexpr int kVStride = (kVRead % 256 <= 64) ? kVRead - kVRead % 256 + 64
                                   : (kVRead % 256 <= 192) ? kVRead - kVRead % 256 + 192
                                                           : kVRead - kVRead % 256 + 320;
-  static constexpr int kKTile = kBN * kKStride;
-  static constexpr int kVTile = kBN * kVStride;
+  static constexpr int kKTile = kStage * kKStride;
+  static constexpr int kVTile = kStage * kVStride;
   static constexpr int kBuf = kKTile + kVTile;  // one stage: K tile then V tile
 };
 
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   float l_part = 0.f;       // this lane's share of the normalizer
 
   const int kend = causal ? min(T, q0 + QT) : T;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int nstages = (kend + kStage - 1) / kStage;
 
   // Tile staging with direct global->LDS loads (global_load_lds_dwordx4, no register
   // staging): one wave instruction writes 64 consecutive 16-byte LDS slots; slot p of a
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   // slots re-read chunk 0 of their row.  In a ragged last tile, rows at or past T read
   // row T-1 instead: those keys are masked, and their finite values meet probability 0.
   constexpr int KP = G_::kKStride / 16, VP = G_::kVStride / 16, C16 = D / 8;
-  constexpr int KI = (KP + kWgWaves - 1) / kWgWaves;  // wave instructions per wave per tile
-  constexpr int VI = (VP + kWgWaves - 1) / kWgWaves;
+  constexpr int KI = (kSub * KP + kWgWaves - 1) / kWgWaves;  // wave instructions per wave per stage
+  constexpr int VI = (kSub * VP + kWgWaves - 1) / kWgWaves;
   int krow[KI], koff[KI], vrow[VI], voff[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
@@ -163,14 +165,14 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto stage = [&](int t, char* dst) {
-    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kBN * D * 2;
-    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kBN * D * 2;
-    const bool ragged = t * kBN + kBN > T;
-    const int rmax = T - 1 - t * kBN;  // last valid row of this tile
+    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kStage * D * 2;
+    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kStage * D * 2;
+    const bool ragged = t * kStage + kStage > T;
+    const int rmax = T - 1 - t * kStage;  // last valid row of this stage
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int inst = wave_u + kWgWaves * i;
-      if (inst < KP) {
+      if (inst < kSub * KP) {
         const int r = ragged ? min(krow[i], rmax) : krow[i];
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(kb + r * (D * 2) + koff[i]),
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int inst = wave_u + kWgWaves * i;
-      if (inst < VP) {
+      if (inst < kSub * VP) {
         const int r = ragged ? min(vrow[i], rmax) : vrow[i];
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(vb + r * (D * 2) + voff[i]),
@@ -194,16 +196,10 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   // and would wait for the loads there), so the next tile's loads are issued after
   // this tile's LDS reads, behind a compiler memory barrier, and overlap the softmax
   // and the P V products.
-  auto step = [&](int t, const char* cur, char* nxt) {
-    const int k0 = t * kBN;
-    // keys k0.. are all beyond this wave's last row: nothing to do (causal)
-    const bool active = !causal || k0 <= qw + 31;
-    const char* kl = cur;
-    const char* vl = cur + G_::kKTile;
-    const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
-    f32x16 s[2];
-    bf16x8 vf[2][2][G_::kDBlocks];
-    if (active) {
+  // One compute tile of 64 keys at k0, in two parts: (A) LDS fragment reads and S^T,
+  // (B) mask, softmax and the P V products.
+  auto part_a = [&](int k0, const char* kl, const char* vl, f32x16 (&s)[2],
+                    bf16x8 (&vf)[2][2][G_::kDBlocks]) {
       // S^T = K Q^T: all K fragments of the tile are read before the matrix ops so
       // the LDS latency is paid once, and the two 32-key blocks form two
       // independent accumulation chains.
@@ -250,10 +246,8 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
           }
       }
 
-    }
-    asm volatile("" ::: "memory");
-    if (t + 1 < ntiles) stage(t + 1, nxt);  // that array was freed by the last barrier
-    if (active) {
+  };
+  auto part_b = [&](int k0, bool diag, f32x16 (&s)[2], const bf16x8 (&vf)[2][2][G_::kDBlocks]) {
       // mask (diagonal tiles only): key j of accumulator r is
       // k0 + 32*sb + 8*(r/4) + 4*half + r%4
       if (diag) {
@@ -316,17 +310,38 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
           for (int kk = 0; kk < 2; ++kk)
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][kk][db], pb[sb][kk], o[db], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
+  };
+  // One LDS stage of kSub compute tiles.  The transposed V reads must not meet
+  // direct-to-LDS loads in flight (the compiler cannot tell them apart and would wait
+  // for the loads there), so the next stage's loads are issued after this stage's last
+  // LDS reads, behind a compiler memory barrier, and overlap the last tile's softmax
+  // and P V products.
+  auto step = [&](int t, const char* cur, char* nxt) {
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int k0 = t * kStage + sub * kBN;
+      // keys k0.. are all beyond this wave's last row, or past T: nothing to do
+      const bool active = (!causal || k0 <= qw + 31) && k0 < T;
+      const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
+      f32x16 s[2];
+      bf16x8 vf[2][2][G_::kDBlocks];
+      if (active) part_a(k0, cur + sub * kBN * G_::kKStride, cur + G_::kKTile + sub * kBN * G_::kVStride, s, vf);
+      if (sub == kSub - 1) {
+        asm volatile("" ::: "memory");
+        if (t + 1 < nstages) stage(t + 1, nxt);  // that array was freed by the last barrier
+      }
+      if (active) part_b(k0, diag, s, vf);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // tile t+1 has landed in LDS
+    __builtin_amdgcn_s_waitcnt(0);  // stage t+1 has landed in LDS
     __syncthreads();
   };
 
   stage(0, lds_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = 0; t < nstages; t += 2) {
     step(t, lds_a, lds_b);
-    if (t + 1 < ntiles) step(t + 1, lds_b, lds_a);
+    if (t + 1 < nstages) step(t + 1, lds_b, lds_a);
   }
 
   // epilogue: O^T row (head dim) of accumulator r in block db is
