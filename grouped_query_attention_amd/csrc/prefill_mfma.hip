@@ -6,10 +6,10 @@
 // row max and normalizer, numerator rescaled as key tiles arrive, no [T, T] buffer.
 //
 // Mapping onto CDNA4:
-//  * A workgroup owns one q-tile of 128 query rows for HPW query heads of the same
-//    K/V group (HPW = 2 when the group has an even number of heads) -- 4*HPW waves,
-//    each wave 32 rows of one head.  The K/V tile (64 keys) is staged once in LDS and
-//    read by every wave: the GQA reuse of "Grouped-Query Attention" section 5.1 lands
+//  * A workgroup of 8 waves owns one q-tile of 256/HPW query rows for HPW query heads
+//    of the same K/V group (HPW = 2 when the group has an even number of heads), each
+//    wave 32 rows of one head.  Each K/V tile is staged once in LDS and read by
+//    every wave: the GQA reuse of "Grouped-Query Attention" section 5.1 lands
 //    in LDS, not in a repeat_interleave copy.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    A = K rows straight from LDS, B = Q^T held in registers for the whole kernel.
@@ -23,8 +23,11 @@
 //  * Online softmax in log2 units (scale*log2(e) folded into one FMA before
 //    v_exp_f32); the running max is only moved when it grows by more than 8, so the
 //    O rescale is skipped on almost every tile (values of p stay below 2^8).
-//  * Causal skipping: tiles (and 32-key halves of tiles) entirely above a wave's
-//    diagonal are not computed; the mask is only evaluated on diagonal tiles.
+//  * K/V rows go from HBM straight into LDS (global_load_lds_dwordx4, no register
+//    staging) in stages of 128 keys, double-buffered in two separate LDS arrays; the
+//    next stage's loads are issued once the current stage's last LDS reads are out.
+//  * Causal skipping: 64-key tiles entirely above a wave's diagonal are not computed;
+//    the mask is only evaluated on diagonal tiles.
 //  * Heaviest q-tiles are dispatched first; blocks of one (batch, head group) keep
 //    the same block-id residue mod 8, i.e. stay on one XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -191,11 +194,6 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     }
   };
 
-  // One tile in two parts around the staging of the next tile.  The transposed V reads
-  // must not meet direct-to-LDS loads in flight (the compiler cannot tell them apart
-  // and would wait for the loads there), so the next tile's loads are issued after
-  // this tile's LDS reads, behind a compiler memory barrier, and overlap the softmax
-  // and the P V products.
   // One compute tile of 64 keys at k0, in two parts: (A) LDS fragment reads and S^T,
   // (B) mask, softmax and the P V products.
   auto part_a = [&](int k0, const char* kl, const char* vl, f32x16 (&s)[2],
