@@ -24,7 +24,8 @@ GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
 
 # every symbol include/gqa_attn.h declares
 EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_decode_workspace_bytes",
-            "attn_decode_num_splits", "attn_decode_cached", "attn_strerror")
+            "attn_decode_num_splits", "attn_decode_cached", "attn_decode_paged_workspace_bytes",
+            "attn_decode_paged", "attn_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgqa_attn.so is not built (%s); run python grouped_query_attention_amd/build.py"
@@ -42,6 +43,11 @@ lib.attn_decode_num_splits.restype = _i
 lib.attn_decode_num_splits.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 lib.attn_decode_cached.restype = _i
 lib.attn_decode_cached.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+lib.attn_decode_paged_workspace_bytes.restype = _sz
+lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+lib.attn_decode_paged.restype = _i
+lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                  _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
@@ -137,4 +143,48 @@ def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, s
                                 ws_ptr, ws_bytes, _stream_handle(stream, q.device))
     if rc != GQA_OK:
         raise GQAError(rc, "attn_decode_cached")
+    return out
+
+
+def attn_decode_paged_workspace_bytes(B, new_tokens, Hq, Hkv, d, block_size, max_blocks,
+                                      dtype=GQA_BF16) -> int:
+    return int(lib.attn_decode_paged_workspace_bytes(B, new_tokens, Hq, Hkv, d, block_size,
+                                                     max_blocks, int(dtype)))
+
+
+def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspace=None,
+                      stream=None):
+    """Paged cached decode.  q [B,n,Hq,d] bf16; kpool, vpool [num_blocks,Hkv,block_size,d]
+    bf16; block_table [B,max_blocks] int32 and seq_lens [B] int32 on the GPU (sequence b's
+    history of seq_lens[b] positions, new tokens last, lives in the blocks its table row
+    names in order).  Scale is 1/sqrt(d).  Returns out [B,n,Hq,d] float32."""
+    B, n, Hq, d = q.shape
+    if kpool.dim() != 4 or kpool.shape[3] != d or vpool.shape != kpool.shape:
+        raise ValueError("kpool, vpool must be [num_blocks, Hkv, block_size, d]; got %s %s"
+                         % (tuple(kpool.shape), tuple(vpool.shape)))
+    if kpool.dtype != q.dtype or vpool.dtype != q.dtype:
+        raise TypeError("q, kpool, vpool must share one dtype")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]; got %s %s"
+                         % (tuple(block_table.shape), tuple(seq_lens.shape)))
+    num_blocks, Hkv, bs = kpool.shape[0], kpool.shape[1], kpool.shape[2]
+    max_blocks = block_table.shape[1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32:
+        raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
+    need = attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.attn_decode_paged(_dev_ptr(q, "q"), _dev_ptr(kpool, "kpool"), _dev_ptr(vpool, "vpool"),
+                               _dev_ptr(block_table, "block_table"), _dev_ptr(seq_lens, "seq_lens"),
+                               _dev_ptr(out, "out"), B, n, Hq, Hkv, d, bs, max_blocks, num_blocks, dt,
+                               ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_decode_paged")
     return out

@@ -52,6 +52,24 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
   return status_of(gqa::launch_attn_generic(a, s));
 }
 
+bool aligned4(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Host-side checks of attn_decode_paged (the device-side table and lengths are checked
+// by the kernels).
+int paged_check(int B, int newTokens, int Hq, int Hkv, int d_h, int block_size, int max_blocks,
+                int num_blocks, int dtype) {
+  int rc = check_common(dtype, B, Hq, Hkv, d_h);
+  if (rc != GQA_OK) return rc;
+  if (newTokens < 0) return GQA_EINVAL;
+  const bool empty = B == 0 || newTokens == 0;
+  if (!empty && (block_size <= 0 || max_blocks <= 0 || num_blocks <= 0)) return GQA_EINVAL;
+  if (block_size < 0 || max_blocks < 0 || num_blocks < 0) return GQA_EINVAL;
+  if ((long long)max_blocks * block_size > kMaxSeq) return GQA_EINVAL;
+  if (dtype != GQA_BF16 || d_h % 16 != 0 || d_h > 128) return GQA_EUNSUPPORTED;
+  if (!empty && block_size % 16 != 0) return GQA_EUNSUPPORTED;
+  return GQA_OK;
+}
+
 int decode_check(int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
                  int dtype) {
   int rc = check_common(dtype, B, Hq, Hkv, d_h);
@@ -118,6 +136,36 @@ int attn_decode_cached(const void* q, const void* kcache, const void* vcache, fl
   gqa::GenericArgs a{q, kcache, vcache, out, dtype, B, Hq, Hkv, newTokens, totalLen, d_h, scale,
                      1, startPos, (long long)newTokens * Hq * sd, sd, (long long)Hq * sd};
   return status_of(gqa::launch_attn_generic(a, s));
+}
+
+size_t attn_decode_paged_workspace_bytes(int B, int newTokens, int Hq, int Hkv, int d_h,
+                                         int block_size, int max_blocks, int dtype) {
+  if (paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, 1, dtype) != GQA_OK)
+    return 0;
+  if (B == 0 || newTokens == 0) return 0;
+  return gqa::plan_decode(B, newTokens, block_size * max_blocks, Hq, Hkv, d_h, dtype).workspace;
+}
+
+int attn_decode_paged(const void* q, const void* kpool, const void* vpool, const int* block_table,
+                      const int* seq_lens, float* out, int B, int newTokens, int Hq, int Hkv,
+                      int d_h, int block_size, int max_blocks, int num_blocks, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, num_blocks, dtype);
+  if (rc != GQA_OK) return rc;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(kpool) || !aligned16(vpool) || !aligned16(out) ||
+      !aligned4(block_table) || !aligned4(seq_lens))
+    return GQA_EINVAL;
+  const int max_len = block_size * max_blocks;
+  const gqa::DecodePlan plan = gqa::plan_decode(B, newTokens, max_len, Hq, Hkv, d_h, dtype);
+  if (!plan.mfma) return GQA_EUNSUPPORTED;
+  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+    return GQA_EWORKSPACE;
+  if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
+  gqa::DecodeArgs a{q, kpool, vpool, out, B, newTokens, Hq, Hkv, max_len, d_h, 0,
+                    1.0f / sqrtf((float)d_h), workspace};
+  gqa::PagedArgs pg{block_table, seq_lens, block_size, max_blocks, num_blocks};
+  return status_of(gqa::launch_attn_decode_paged(a, pg, plan, static_cast<hipStream_t>(stream)));
 }
 
 const char* attn_strerror(int code) {

@@ -56,6 +56,18 @@ struct DGeo {
   static constexpr int kLdsPerWave = kTile * kVStride;
 };
 
+// Where the K/V history lives: one contiguous [B, Hkv, L, d] cache, or a pool of
+// blocks [num_blocks, Hkv, bs, d] addressed through a per-sequence block table.
+struct KvSource {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* table;  // paged: [B, max_blocks] physical block of each logical block
+  const int* lens;   // paged: [B] history length of each sequence (new tokens included)
+  int L;             // contiguous: rows per head in the cache
+  int start_pos;     // contiguous: position of the first new token (every sequence)
+  int bs, max_blocks, num_blocks, max_len;  // paged
+};
+
 __device__ __forceinline__ float xmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // reduce over the 4 lane groups (lanes l, l^16, l^32, l^48 hold the same query column)
@@ -70,11 +82,10 @@ __device__ __forceinline__ float group_sum(float x) {
   return x + __shfl_xor(x, 16);
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, float* __restrict__ opart, float* __restrict__ mlpart, int n,
-    int Hq, int Hkv, int L, int start_pos, float c, int nsplit, int chunk, int ncb,
+    const uint16_t* __restrict__ q, const KvSource kv, float* __restrict__ opart,
+    float* __restrict__ mlpart, int n, int Hq, int Hkv, float c, int nsplit, int chunk, int ncb,
     int total_waves) {
   using G_ = DGeo<D>;
   __shared__ __attribute__((aligned(16))) char smem[kWaves * G_::kLdsPerWave];
@@ -91,7 +102,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
   const int b = bg / Hkv;
   const int G = Hq / Hkv;
   const int ncols = G * n;
-  const int kv_len = start_pos + n;  // keys any new token can see
+  int kv_len;  // keys any new token can see: the sequence's history length
+  if constexpr (PAGED) {
+    kv_len = kv.lens[b];
+    if (kv_len < n || kv_len > kv.max_len) return;  // the merge marks the sequence's rows
+  } else {
+    kv_len = kv.start_pos + n;
+  }
+  const int start_pos = kv_len - n;
+  const int last = kv_len - 1;  // rows past it are never read
   const int c0 = split * chunk;
   if (c0 >= kv_len) return;  // empty chunk: the merge only reads chunks below kv_len
   const int c1 = min(c0 + chunk, kv_len);
@@ -115,33 +134,70 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
     qf[st] = __builtin_bit_cast(bf16x8, x);
   }
 
-  const long long kv_base = ((long long)b * Hkv + g) * (long long)L * D;
-  const uint16_t* kg = kc + kv_base;
-  const uint16_t* vg = vc + kv_base;
+  // Where a 32-key tile's rows live.  A tile is two 16-row groups; group kb covers rows
+  // j0+16kb .. j0+16kb+15, clamped to `last`.  Rows of one group are consecutive in
+  // memory: in the contiguous cache trivially, in a pool because a block holds a
+  // multiple of 16 positions.  rows[kb] is the element offset of the group's first
+  // (clamped) row; row r of the group is at rows[kb] + (min(j0+16kb+r, last) - first)*D.
+  const long long head_base = ((long long)b * Hkv + g) * (long long)kv.L * D;  // contiguous
+  const int* tab = PAGED ? kv.table + (long long)b * kv.max_blocks : nullptr;
+  bool bad = false;  // a table entry outside the pool: the sequence's rows become NaN
+  // table entries of a tile's two groups; fetched one tile ahead of the K/V loads with
+  // vector loads (a scalar load would share its wait counter with the LDS traffic)
+  auto fetch = [&](int j0, int (&e)[2]) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        int blk = min(j0 + 16 * kb, last) / kv.bs;
+        asm volatile("" : "+v"(blk));  // keep the address per lane: a vector load
+        e[kb] = tab[blk];
+      }
+    }
+  };
+  auto resolve = [&](int j0, const int (&e)[2], long long (&rows)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int first = min(j0 + 16 * kb, last);
+      if constexpr (PAGED) {
+        int ent = __builtin_amdgcn_readfirstlane(e[kb]);
+        if (ent < 0 || ent >= kv.num_blocks) {
+          bad = true;
+          ent = 0;
+        }
+        rows[kb] = (((long long)ent * Hkv + g) * kv.bs + first % kv.bs) * D;
+      } else {
+        rows[kb] = head_base + (long long)first * D;
+      }
+    }
+  };
   char* vl = smem + wave * G_::kLdsPerWave;
 
   // K fragments of a tile (A operand): block kb, step st -> key j0 + 16kb + col,
-  // head dims 32st + 8grp .. +7.  Keys past the cache end are clamped (masked anyway).
-  auto load_k = [&](int j0, bf16x8 (&kf)[2][G_::kSteps]) {
+  // head dims 32st + 8grp .. +7.
+  auto load_k = [&](int j0, const long long (&rows)[2], bf16x8 (&kf)[2][G_::kSteps]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const long long row = (long long)min(j0 + 16 * kb + col, L - 1) * D;
+      const int first = min(j0 + 16 * kb, last);
+      const long long row = rows[kb] + (long long)(min(j0 + 16 * kb + col, last) - first) * D;
 #pragma unroll
       for (int st = 0; st < G_::kSteps; ++st) {
         const int d0 = 32 * st + 8 * grp;
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (d0 < D) x = *reinterpret_cast<const u32x4*>(kg + row + d0);
+        if (d0 < D) x = *reinterpret_cast<const u32x4*>(kv.k + row + d0);
         kf[kb][st] = __builtin_bit_cast(bf16x8, x);
       }
     }
   };
   // V tile rows j0..j0+31, contiguous 16-byte chunks per lane (4 rows per 1 KB load)
-  auto load_v = [&](int j0, u32x4 (&vr)[G_::kPerLane]) {
+  auto load_v = [&](int j0, const long long (&rows)[2], u32x4 (&vr)[G_::kPerLane]) {
 #pragma unroll
     for (int i = 0; i < G_::kPerLane; ++i) {
       const int ch = lane + 64 * i;
       const int r = ch / (D / 8), cc = ch % (D / 8);
-      vr[i] = *reinterpret_cast<const u32x4*>(vg + (long long)min(j0 + r, L - 1) * D + cc * 8);
+      const int kb = r >> 4;
+      const int first = min(j0 + 16 * kb, last);
+      const long long row = (kb ? rows[1] : rows[0]) + (long long)(min(j0 + r, last) - first) * D;
+      vr[i] = *reinterpret_cast<const u32x4*>(kv.v + row + cc * 8);
     }
   };
   auto store_v = [&](const u32x4 (&vr)[G_::kPerLane]) {
@@ -166,15 +222,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
 
   bf16x8 kf[2][G_::kSteps];
   u32x4 vr[G_::kPerLane];
-  load_k(c0, kf);
-  load_v(c0, vr);
+  int ent[2] = {0, 0}, ent_next[2] = {0, 0};
+  long long rows[2];
+  fetch(c0, ent);
+  resolve(c0, ent, rows);
+  load_k(c0, rows, kf);
+  load_v(c0, rows, vr);
+  if (c0 + kTile < c1) fetch(c0 + kTile, ent_next);
   for (int j0 = c0; j0 < c1; j0 += kTile) {
     store_v(vr);  // this wave's earlier reads of the tile buffer are complete
     bf16x8 kn[2][G_::kSteps];
     const bool more = j0 + kTile < c1;
     if (more) {
-      load_k(j0 + kTile, kn);
-      load_v(j0 + kTile, vr);
+      resolve(j0 + kTile, ent_next, rows);
+      load_k(j0 + kTile, rows, kn);
+      load_v(j0 + kTile, rows, vr);
+      if (j0 + 2 * kTile < c1) fetch(j0 + 2 * kTile, ent_next);
     }
 
     f32x4 s[2];
@@ -244,8 +307,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
   }
 
   // partial (m, l, O) of this chunk for every valid column.  O^T row (head dim) of
-  // accumulator r in block db is 16db + 4grp + r.
-  const float l_tot = group_sum(l_part);
+  // accumulator r in block db is 16db + 4grp + r.  A bad table entry poisons the
+  // chunk (m = l = NaN), and the merge carries the NaN into every row of the group.
+  float l_tot = group_sum(l_part);
+  if (bad) {
+    m_run = __builtin_nanf("");
+    l_tot = __builtin_nanf("");
+  }
   if (col_ok) {
     const long long pidx = ((long long)(b * Hkv + g) * nsplit + split) * ncols + cidx;
     float* op = opart + pidx * D;
@@ -260,11 +328,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
 }
 
 // One 64-thread block per output row (b, g, column): combine the chunk partials.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ opart,
                                                           const float* __restrict__ mlpart,
-                                                          float* __restrict__ out, int n, int Hq,
-                                                          int Hkv, int nsplit, int nvalid) {
+                                                          float* __restrict__ out, const KvSource kv,
+                                                          int n, int Hq, int Hkv, int nsplit,
+                                                          int chunk) {
   constexpr int PER = (D + 63) / 64;
   const int G = Hq / Hkv;
   const int ncols = G * n;
@@ -273,6 +342,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   const int bg = row / ncols;
   const int g = bg % Hkv, b = bg / Hkv;
   const int tok = cidx / G, hq = g * G + cidx % G;
+  float* orow = out + (((long long)b * n + tok) * Hq + hq) * D;
+  int kv_len;
+  if constexpr (PAGED) {
+    kv_len = kv.lens[b];
+    if (kv_len < n || kv_len > kv.max_len) {  // no valid history: the row is NaN
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int d = threadIdx.x + 64 * e;
+        if (d < D) orow[d] = __builtin_nanf("");
+      }
+      return;
+    }
+  } else {
+    kv_len = kv.start_pos + n;
+  }
+  const int nvalid = (kv_len + chunk - 1) / chunk;
   const long long base = (long long)bg * nsplit * ncols + cidx;  // partial index of split 0
 
   float M = -INFINITY;
@@ -291,7 +376,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     }
   }
   const float inv = 1.f / Lsum;
-  float* orow = out + (((long long)b * n + tok) * Hq + hq) * D;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int d = threadIdx.x + 64 * e;
@@ -299,8 +383,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   }
 }
 
-template <int D>
-hipError_t launch_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+template <int D, bool PAGED>
+hipError_t launch_d(const DecodeArgs& a, const KvSource& kv, const DecodePlan& p,
+                    hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int ncols = G * a.n;
   const int ncb = (ncols + kCols - 1) / kCols;
@@ -311,17 +396,30 @@ hipError_t launch_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream
   float* mlpart = opart + np * D;
   const float c = a.scale * 1.4426950408889634f;
   const int blocks = (int)((total + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(blocks), dim3(kWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
-                     static_cast<const uint16_t*>(a.vc), opart, mlpart, a.n, a.Hq, a.Hkv, a.L,
-                     a.start_pos, c, p.nsplit, p.chunk, ncb, (int)total);
+  hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3(blocks), dim3(kWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(a.q), kv, opart, mlpart, a.n, a.Hq, a.Hkv, c,
+                     p.nsplit, p.chunk, ncb, (int)total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int kv_len = a.start_pos + a.n;
-  const int nvalid = (kv_len + p.chunk - 1) / p.chunk;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * ncols), dim3(64), 0, stream,
-                     opart, mlpart, a.out, a.n, a.Hq, a.Hkv, p.nsplit, nvalid);
+  hipLaunchKernelGGL((decode_merge_kernel<D, PAGED>), dim3(a.B * a.Hkv * ncols), dim3(64), 0,
+                     stream, opart, mlpart, a.out, kv, a.n, a.Hq, a.Hkv, p.nsplit, p.chunk);
   return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_any_d(const DecodeArgs& a, const KvSource& kv, const DecodePlan& p,
+                        hipStream_t stream) {
+  switch (a.d) {
+    case 16: return launch_d<16, PAGED>(a, kv, p, stream);
+    case 32: return launch_d<32, PAGED>(a, kv, p, stream);
+    case 48: return launch_d<48, PAGED>(a, kv, p, stream);
+    case 64: return launch_d<64, PAGED>(a, kv, p, stream);
+    case 80: return launch_d<80, PAGED>(a, kv, p, stream);
+    case 96: return launch_d<96, PAGED>(a, kv, p, stream);
+    case 112: return launch_d<112, PAGED>(a, kv, p, stream);
+    case 128: return launch_d<128, PAGED>(a, kv, p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -348,17 +446,17 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
 }
 
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
-  switch (a.d) {
-    case 16: return launch_d<16>(a, p, stream);
-    case 32: return launch_d<32>(a, p, stream);
-    case 48: return launch_d<48>(a, p, stream);
-    case 64: return launch_d<64>(a, p, stream);
-    case 80: return launch_d<80>(a, p, stream);
-    case 96: return launch_d<96>(a, p, stream);
-    case 112: return launch_d<112>(a, p, stream);
-    case 128: return launch_d<128>(a, p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), nullptr,
+              nullptr, a.L, a.start_pos, 0, 0, 0, 0};
+  return launch_any_d<false>(a, kv, p, stream);
+}
+
+hipError_t launch_attn_decode_paged(const DecodeArgs& a, const PagedArgs& pg, const DecodePlan& p,
+                                    hipStream_t stream) {
+  KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), pg.table,
+              pg.seq_lens, 0, 0, pg.block_size, pg.max_blocks, pg.num_blocks,
+              pg.block_size * pg.max_blocks};
+  return launch_any_d<true>(a, kv, p, stream);
 }
 
 }  // namespace gqa

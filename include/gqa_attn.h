@@ -100,7 +100,8 @@ int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, 
  *                     Hesper KV cache layout), with the new tokens' K/V already written at
  *                     positions startPos .. startPos+newTokens-1
  *   startPos        : absolute position of the first new token; new token i attends to
- *                     keys 0 .. startPos+i
+ *                     keys 0 .. startPos+i (cache rows at or past startPos+newTokens are
+ *                     never read, so a larger preallocated cache may hold anything there)
  *   scale           : fixed at 1/sqrt(d_h), as in CausalAttentionCached
  *   workspace       : device buffer of at least attn_decode_workspace_bytes(...) bytes
  *                     (may be NULL when that is 0); contents on entry are ignored
@@ -113,6 +114,51 @@ int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, 
 int attn_decode_cached(const void* q, const void* kcache, const void* vcache, float* out,
                        int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_paged needs (0 when it needs none).  The key
+ * split is planned for the longest history the table can describe,
+ * max_blocks * block_size.  Pure host arithmetic; 0 for arguments attn_decode_paged
+ * would reject.
+ */
+size_t attn_decode_paged_workspace_bytes(int B, int newTokens, int Hq, int Hkv, int d_h,
+                                         int block_size, int max_blocks, int dtype);
+
+/*
+ * Paged (block-table) cached decode: makarna's CausalAttentionPackedBlocks, and the
+ * "paged decode attention" of the Hesper-style backend notes (one new-token query
+ * block reading a logical-to-physical K/V page table).  Per sequence b it computes
+ * exactly attn_decode_cached over the history its blocks hold.
+ *
+ *   q, out          : [B, newTokens, Hq, d_h]  as in attn_decode_cached
+ *   kpool, vpool    : [num_blocks, Hkv, block_size, d_h]  physical blocks; inside a block
+ *                     the layout is head-major, [kvHead][tokenWithinBlock][headDim] (the
+ *                     packed view layout)
+ *   block_table     : [B, max_blocks] int32, DEVICE memory.  Logical block i of sequence b
+ *                     (positions i*block_size .. i*block_size+block_size-1) is physical
+ *                     block block_table[b*max_blocks + i].  Entries past the last block a
+ *                     sequence needs are never read; blocks may be shared by sequences.
+ *   seq_lens        : [B] int32, DEVICE memory.  History length of sequence b, new tokens
+ *                     included: its new tokens sit at positions seq_lens[b]-newTokens ..
+ *                     seq_lens[b]-1, and new token i attends to keys 0 .. seq_lens[b]-
+ *                     newTokens+i.  Slots of a block past seq_lens[b] are never read.
+ *   scale           : fixed at 1/sqrt(d_h)
+ *   workspace       : at least attn_decode_paged_workspace_bytes(...) bytes
+ *
+ * Supported: dtype GQA_BF16 with d_h a multiple of 16 up to 128, block_size a positive
+ * multiple of 16 (else GQA_EUNSUPPORTED).  Host-side errors as attn_decode_cached, plus
+ * GQA_EINVAL for block_size, max_blocks or num_blocks <= 0 on a non-empty call,
+ * max_blocks * block_size above 2^30, and NULL or misaligned table/lengths (4-byte
+ * alignment).  The table and lengths live on the device and are checked by the kernels:
+ * a sequence whose length is below newTokens or above max_blocks*block_size, or whose
+ * needed table entries fall outside [0, num_blocks), gets NaN in all of its output
+ * rows, and nothing outside the pools is read.
+ */
+int attn_decode_paged(const void* q, const void* kpool, const void* vpool,
+                      const int* block_table, const int* seq_lens, float* out, int B,
+                      int newTokens, int Hq, int Hkv, int d_h, int block_size, int max_blocks,
+                      int num_blocks, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* attn_strerror(int code);

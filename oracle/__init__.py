@@ -17,6 +17,8 @@ mask"), the "Grouped-Query Attention" chapter (sections 5.1 and 5.2) and, for
 cached decode, makarna's ``CausalAttentionCached``: the new tokens sit at
 absolute positions startPos .. startPos+newTokens-1, each sees every cached key
 up to and including its own position, and the scale is 1/sqrt(headDim).
+Paged decode (makarna's ``CausalAttentionPackedBlocks``) is that same cached
+decode over the history assembled from the blocks a block table names.
 
 Inputs are widened exactly to float64 (bf16 and fp32 values are all exactly
 representable), so the oracle never rounds an input.
@@ -125,6 +127,53 @@ def decode_cached(q, kcache, vcache, start_pos: int, nthreads: int = 0):
     d = qh.shape[-1]
     out = attention(qh, kcache, vcache, 1.0 / math.sqrt(d), True, start_pos, nthreads)
     return np.ascontiguousarray(out.transpose(0, 2, 1, 3))
+
+
+def gather_paged(pool, block_table, seq_len: int, block_size: int, b: int):
+    """The logical K (or V) history of sequence b out of a block pool.
+
+    pool: [num_blocks, Hkv, block_size, d], head-major inside each block (makarna's
+    packed view layout [kvHead][tokenWithinBlock][headDim]).  Logical block i of the
+    sequence is the view with Start = i * block_size and Length = min(block_size,
+    seq_len - Start); its physical block is block_table[b][i].  Table entries past the
+    last block the sequence needs are never read.  Returns [Hkv, seq_len, d] (float64).
+    """
+    pool = to_f64(pool)
+    nb, hkv, bs, d = pool.shape
+    if bs != block_size:
+        raise ValueError("pool block size %d != block_size %d" % (bs, block_size))
+    nblk = -(-seq_len // block_size)
+    table = np.asarray(block_table)
+    if nblk > table.shape[1]:
+        raise ValueError("sequence %d needs %d blocks, table has %d" % (b, nblk, table.shape[1]))
+    ids = [int(x) for x in table[b, :nblk]]
+    if any(i < 0 or i >= nb for i in ids):
+        raise ValueError("sequence %d: block id out of range" % b)
+    hist = np.empty((hkv, nblk * block_size, d), dtype=np.float64)
+    for i, blk in enumerate(ids):  # view i covers positions i*bs .. i*bs+bs-1
+        hist[:, i * block_size:(i + 1) * block_size, :] = pool[blk]
+    return hist[:, :seq_len, :]
+
+
+def decode_paged(q, kpool, vpool, block_table, seq_lens, block_size: int, nthreads: int = 0):
+    """Paged (block-table) cached decode: the cached decode of every sequence b over
+    the history gather_paged assembles, with its own length seq_lens[b] (new tokens
+    at seq_lens[b]-n .. seq_lens[b]-1).  q [B,n,Hq,d] -> out [B,n,Hq,d] (float64).
+    This is makarna's CausalAttentionPackedBlocks with one view per table entry.
+    """
+    q = to_f64(q)
+    B, n, Hq, d = q.shape
+    out = np.zeros((B, n, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < n:
+            raise ValueError("sequence %d: length %d < newTokens %d" % (b, L, n))
+        if n == 0:
+            continue
+        kh = gather_paged(kpool, block_table, L, block_size, b)
+        vh = gather_paged(vpool, block_table, L, block_size, b)
+        out[b] = decode_cached(q[b:b + 1], kh[None], vh[None], L - n, nthreads)[0]
+    return out
 
 
 def probs(q, k, v, scale: float, causal: bool = True, pos0: int = 0):

@@ -141,3 +141,75 @@ def decode_inputs(B, n, Hq, Hkv, total_len, d, dtype, seed, device="cpu"):
 def decode_config_inputs(cfg: DecodeConfig, device="cpu"):
     return decode_inputs(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.total_len, cfg.d, cfg.dtype, cfg.seed,
                          device)
+
+
+# ---- paged (block-table) decode -------------------------------------------------------
+
+def blocks_needed(seq_len: int, block_size: int) -> int:
+    return -(-seq_len // block_size)
+
+
+def paged_layout(seq_lens, block_size: int, max_blocks: int, seed: int, spare_blocks: int = 0):
+    """Block table of a fragmented pool: the blocks every sequence needs, plus
+    `spare_blocks` unused ones, are handed out in a seeded random order.  Entries past a
+    sequence's last block are -1.  Returns (table [B, max_blocks] int32, num_blocks)."""
+    need = [blocks_needed(int(L), block_size) for L in seq_lens]
+    if max(need, default=0) > max_blocks:
+        raise ValueError("a sequence needs more than max_blocks blocks")
+    num_blocks = sum(need) + spare_blocks
+    gen = torch.Generator("cpu").manual_seed(seed * 7 + 3)
+    perm = torch.randperm(max(num_blocks, 1), generator=gen)[:num_blocks]
+    table = torch.full((len(seq_lens), max_blocks), -1, dtype=torch.int32)
+    at = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[at:at + nb].to(torch.int32)
+        at += nb
+    return table, num_blocks
+
+
+def scatter_history(pool, table_row, hist, block_size: int):
+    """Write one sequence's history hist [Hkv, L, d] into its blocks of pool
+    [num_blocks, Hkv, block_size, d] (pool and hist on the same device)."""
+    Hkv, L, d = hist.shape
+    nb = blocks_needed(L, block_size)
+    for i in range(nb):
+        lo, hi = i * block_size, min(L, (i + 1) * block_size)
+        pool[int(table_row[i]), :, :hi - lo, :] = hist[:, lo:hi, :]
+
+
+def paged_decode_inputs(B, n, Hq, Hkv, d, block_size, seq_lens, max_blocks, dtype, seed,
+                        device="cpu", spare_blocks=0, fill=float("nan")):
+    """q [B,n,Hq,d]; kpool, vpool [num_blocks,Hkv,block_size,d]; table [B,max_blocks]
+    int32; lens [B] int32.  Sequence b's history is decode_cache_chunk(seed, tensor, b,
+    Hkv, seq_lens[b], d, dtype): a sequence whose length equals a contiguous cache's
+    total_len holds exactly that cache's values.  Pool slots that no sequence owns hold
+    `fill`."""
+    q = decode_query(B, n, Hq, d, dtype, seed).to(device)
+    table, num_blocks = paged_layout(seq_lens, block_size, max_blocks, seed, spare_blocks)
+    kpool = torch.full((num_blocks, Hkv, block_size, d), fill, dtype=torch_dtype(dtype), device=device)
+    vpool = torch.full_like(kpool, fill)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for tid, pool in ((0, kpool), (1, vpool)):
+            hist = decode_cache_chunk(seed, tid, b, Hkv, L, d, dtype).to(device)
+            scatter_history(pool, table[b], hist, block_size)
+    lens = torch.tensor([int(L) for L in seq_lens], dtype=torch.int32)
+    return q, kpool, vpool, table.to(device), lens.to(device)
+
+
+def paged_from_contiguous(kc, vc, block_size: int, seed: int):
+    """Pools, table and lengths holding exactly the contiguous caches kc, vc [B,Hkv,L,d]
+    (L a multiple of block_size), blocks in a seeded random order; built on kc's device."""
+    B, Hkv, L, d = kc.shape
+    if L % block_size:
+        raise ValueError("L must be a multiple of block_size")
+    nblk = L // block_size
+    table, nb = paged_layout([L] * B, block_size, nblk, seed)
+    idx = table.reshape(-1).to(device=kc.device, dtype=torch.long)
+    pools = []
+    for c in (kc, vc):
+        pool = torch.empty((nb, Hkv, block_size, d), dtype=c.dtype, device=c.device)
+        pool[idx] = c.view(B, Hkv, nblk, block_size, d).transpose(1, 2).reshape(B * nblk, Hkv, block_size, d)
+        pools.append(pool)
+    lens = torch.full((B,), L, dtype=torch.int32, device=kc.device)
+    return pools[0], pools[1], table.to(kc.device), lens

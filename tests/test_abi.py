@@ -130,3 +130,57 @@ def test_decode_plan_host_logic():
     # invalid shapes plan nothing
     assert gqa.attn_decode_num_splits(1, 2, 1, 4, 1, 64, BF16) == 0
     assert gqa.attn_decode_workspace_bytes(1, 1, 8, 3, 2, 64, BF16) == 0
+
+
+A4 = 0x10004  # 4-byte aligned, not 16-byte aligned
+
+
+def paged(q=A16, kp=A16, vp=A16, table=A16, lens=A16, out=A16, B=2, n=1, Hq=4, Hkv=1, d=64, bs=16,
+          max_blocks=8, num_blocks=16, dtype=BF16, ws=A16, ws_bytes=1 << 30):
+    return lib.attn_decode_paged(q, kp, vp, table, lens, out, B, n, Hq, Hkv, d, bs, max_blocks,
+                                 num_blocks, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(Hq=6, Hkv=4), EINVAL),
+    (dict(Hkv=0), EINVAL),
+    (dict(bs=0), EINVAL),
+    (dict(bs=-16), EINVAL),
+    (dict(max_blocks=0), EINVAL),
+    (dict(num_blocks=0), EINVAL),
+    (dict(bs=1 << 20, max_blocks=1 << 11), EINVAL),  # history longer than 2^30
+    (dict(bs=24), EUNSUP),                           # block size not a multiple of 16
+    (dict(dtype=F32), EUNSUP),                       # bf16 pools only
+    (dict(d=72), EUNSUP),
+    (dict(d=144), EUNSUP),
+    (dict(dtype=5), EINVAL),
+    (dict(table=None), EINVAL),
+    (dict(lens=A16 + 2), EINVAL),
+    (dict(kp=A4), EINVAL),
+    (dict(out=None), EINVAL),
+])
+def test_paged_rejects(kw, code):
+    assert paged(**kw) == code
+
+
+def test_paged_table_and_lengths_need_only_4_byte_alignment():
+    # validation passes with 4-byte aligned metadata; an empty call then does nothing
+    assert paged(table=A4, lens=A4, B=0) == OK
+    assert paged(q=None, kp=None, vp=None, table=None, lens=None, out=None, n=0) == OK
+    assert paged(q=None, kp=None, vp=None, table=None, lens=None, out=None, B=0, bs=0,
+                 max_blocks=0, num_blocks=0) == OK
+
+
+def test_paged_workspace_checked_before_launch():
+    B, n, Hq, Hkv, d, bs, mb = 64, 4, 32, 8, 128, 16, 2048
+    need = gqa.attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, mb, BF16)
+    assert need == gqa.attn_decode_workspace_bytes(B, n, bs * mb, Hq, Hkv, d, BF16) > 0
+    args = dict(B=B, n=n, Hq=Hq, Hkv=Hkv, d=d, bs=bs, max_blocks=mb, num_blocks=B * mb)
+    assert paged(ws=None, ws_bytes=need, **args) == EWS
+    assert paged(ws=A16, ws_bytes=need - 1, **args) == EWS
+    assert paged(ws=A16 + 8, ws_bytes=need, **args) == EINVAL
+    # rejected shapes need nothing
+    assert gqa.attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, 24, mb, BF16) == 0
+    assert gqa.attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, mb, F32) == 0

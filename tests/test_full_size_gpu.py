@@ -80,3 +80,29 @@ def test_full_size_decode_sampled_units(gqa, decode_data, cfg):
         worst = max(worst, float(np.abs(got - want).max()))
     print("%s sampled max-abs error %.3g" % (cfg.name, worst))
     assert worst <= TOL[cfg.dtype], worst
+
+
+@pytest.mark.parametrize("cfg", [si.C5_DECODE_N1, si.C5_DECODE_N4], ids=lambda c: c.name)
+def test_full_size_paged_decode(gqa, decode_data, cfg):
+    """The same cache scattered into 16-position blocks in a random order: attn_decode_paged
+    must give exactly attn_decode_cached's result (same kernels and split plan), and match
+    the oracle on a sampled unit."""
+    kc, vc = decode_data
+    bs = 16
+    print("paged pools for", cfg.name, flush=True)
+    kp, vp, table, lens = si.paged_from_contiguous(kc, vc, bs, cfg.seed)
+    q = si.decode_query(cfg.B, cfg.n, cfg.Hq, cfg.d, cfg.dtype, cfg.seed)
+    a = gqa.attn_decode_cached(q.cuda(), kc, vc, cfg.start_pos)
+    p = gqa.attn_decode_paged(q.cuda(), kp, vp, table, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a, p)
+    G = cfg.Hq // cfg.Hkv
+    b, g = 21, 3
+    kb = si.decode_cache_chunk(cfg.seed, 0, b, cfg.Hkv, cfg.total_len, cfg.d, cfg.dtype)[g]
+    vb = si.decode_cache_chunk(cfg.seed, 1, b, cfg.Hkv, cfg.total_len, cfg.d, cfg.dtype)[g]
+    heads = slice(g * G, (g + 1) * G)
+    want = oracle.decode_cached(q[b:b + 1, :, heads], kb[None, None], vb[None, None], cfg.start_pos)
+    err = float(np.abs(p[b:b + 1, :, heads].cpu().double().numpy() - want).max())
+    print("%s paged sampled max-abs error %.3g" % (cfg.name, err))
+    assert err <= TOL[cfg.dtype], err
+    del kp, vp
