@@ -55,15 +55,15 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=False)
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_attention.restype = ctypes.c_int
         dp = ctypes.POINTER(ctypes.c_double)
         lib.oracle_attention.argtypes = [dp, dp, dp, dp, dp,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
-                                         ctypes.c_long, ctypes.c_int]
+                                         ctypes.c_long, ctypes.c_long, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         _lib = lib
@@ -90,11 +90,12 @@ def default_threads() -> int:
 
 
 def attention(q, k, v, scale: float, causal: bool = True, pos0: int = 0,
-              nthreads: int = 0, want_probs: bool = False):
+              nthreads: int = 0, want_probs: bool = False, window: int = 0):
     """Materialized float64 attention in head-major layout.
 
     q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d].  Query row i is at absolute
-    position pos0 + i.  Returns out [B, Hq, Tq, d] (float64), and P
+    position pos0 + i.  window >= 1 (causal only) keeps keys pos0+i-window+1 ..
+    pos0+i; 0 means no window.  Returns out [B, Hq, Tq, d] (float64), and P
     [B, Hq, Tq, Tk] as well when want_probs.
     """
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
@@ -106,26 +107,29 @@ def attention(q, k, v, scale: float, causal: bool = True, pos0: int = 0,
     probs = np.zeros((B, Hq, Tq, Tk), dtype=np.float64) if want_probs else None
     rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(probs),
                                   B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)),
-                                  int(pos0), int(nthreads))
+                                  int(pos0), int(window), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments (rc=%d)" % rc)
     return (out, probs) if want_probs else out
 
 
-def prefill(q, k, v, scale: float, causal: bool = True, nthreads: int = 0):
-    """Full-sequence prefill: q [B,Hq,T,d], k/v [B,Hkv,T,d] -> out [B,Hq,T,d]."""
-    return attention(q, k, v, scale, causal, 0, nthreads)
+def prefill(q, k, v, scale: float, causal: bool = True, nthreads: int = 0, window: int = 0):
+    """Full-sequence prefill: q [B,Hq,T,d], k/v [B,Hkv,T,d] -> out [B,Hq,T,d].
+    window >= 1: local causal attention over the last `window` positions."""
+    return attention(q, k, v, scale, causal, 0, nthreads, window=window)
 
 
-def decode_cached(q, kcache, vcache, start_pos: int, nthreads: int = 0):
+def decode_cached(q, kcache, vcache, start_pos: int, nthreads: int = 0, window: int = 0):
     """Cached decode: q [B,n,Hq,d] (new tokens, token-major like makarna's Q),
     kcache/vcache [B,Hkv,totalLen,d] already holding the new tokens at
     start_pos..start_pos+n-1.  Scale is 1/sqrt(d) as in CausalAttentionCached.
+    window >= 1: token i sees keys start_pos+i-window+1 .. start_pos+i only.
     Returns out [B,n,Hq,d] (float64).
     """
     qh = to_f64(q).transpose(0, 2, 1, 3)  # layout change only: [B,Hq,n,d]
     d = qh.shape[-1]
-    out = attention(qh, kcache, vcache, 1.0 / math.sqrt(d), True, start_pos, nthreads)
+    out = attention(qh, kcache, vcache, 1.0 / math.sqrt(d), True, start_pos, nthreads,
+                    window=window)
     return np.ascontiguousarray(out.transpose(0, 2, 1, 3))
 
 
@@ -155,7 +159,8 @@ def gather_paged(pool, block_table, seq_len: int, block_size: int, b: int):
     return hist[:, :seq_len, :]
 
 
-def decode_paged(q, kpool, vpool, block_table, seq_lens, block_size: int, nthreads: int = 0):
+def decode_paged(q, kpool, vpool, block_table, seq_lens, block_size: int, nthreads: int = 0,
+                 window: int = 0):
     """Paged (block-table) cached decode: the cached decode of every sequence b over
     the history gather_paged assembles, with its own length seq_lens[b] (new tokens
     at seq_lens[b]-n .. seq_lens[b]-1).  q [B,n,Hq,d] -> out [B,n,Hq,d] (float64).
@@ -172,10 +177,10 @@ def decode_paged(q, kpool, vpool, block_table, seq_lens, block_size: int, nthrea
             continue
         kh = gather_paged(kpool, block_table, L, block_size, b)
         vh = gather_paged(vpool, block_table, L, block_size, b)
-        out[b] = decode_cached(q[b:b + 1], kh[None], vh[None], L - n, nthreads)[0]
+        out[b] = decode_cached(q[b:b + 1], kh[None], vh[None], L - n, nthreads, window)[0]
     return out
 
 
-def probs(q, k, v, scale: float, causal: bool = True, pos0: int = 0):
+def probs(q, k, v, scale: float, causal: bool = True, pos0: int = 0, window: int = 0):
     """The probability matrix P [B,Hq,Tq,Tk] (small shapes only)."""
-    return attention(q, k, v, scale, causal, pos0, 1, want_probs=True)[1]
+    return attention(q, k, v, scale, causal, pos0, 1, want_probs=True, window=window)[1]

@@ -23,6 +23,10 @@
  *
  *   allowed(i,j) = !causal || j <= p_i     (Hesper "Causal Masking": 0 on and
  *                                           below the diagonal, -inf above)
+ *                  and, with a local window W >= 1 (causal only),
+ *                  j >= p_i - W + 1        (the multi-query primer's local
+ *                                           attention, section 4.1: the current
+ *                                           position and the W-1 before it)
  *   s_ij = scale * sum_d q[b,h,i,d] * k[b,g,j,d]
  *                                          (Riftco "Dataflow and shapes":
  *                                           scores = Q K^T / sqrt(d_h))
@@ -57,10 +61,18 @@ typedef struct {
     double *probs; /* [B,Hq,Tq,Tk] probabilities, or NULL */
     int B, Hq, Hkv, Tq, Tk, d, causal;
     long pos0;
+    long window; /* 0: no window */
     double scale;
     int nthreads;
     int tid;
 } job_t;
+
+/* The mask: may query position p see key j? */
+static int allowed(const job_t *J, long p, long j) {
+    if (J->causal && j > p) return 0;
+    if (J->window > 0 && j < p - J->window + 1) return 0;
+    return 1;
+}
 
 /* One (b, h) unit: every query row of query head h in batch b. */
 static void run_unit(const job_t *J, int b, int h, double *row) {
@@ -76,8 +88,7 @@ static void run_unit(const job_t *J, int b, int h, double *row) {
         /* scores of the allowed keys; the row is materialized in full */
         double m = -INFINITY;
         for (int j = 0; j < Tk; ++j) {
-            const int allowed = !J->causal || (long)j <= p;
-            if (!allowed) {
+            if (!allowed(J, p, j)) {
                 row[j] = -INFINITY; /* additive -inf mask */
                 continue;
             }
@@ -91,8 +102,7 @@ static void run_unit(const job_t *J, int b, int h, double *row) {
         /* softmax over the key axis: masked entries are exactly zero */
         double denom = 0.0;
         for (int j = 0; j < Tk; ++j) {
-            const int allowed = !J->causal || (long)j <= p;
-            row[j] = allowed ? exp(row[j] - m) : 0.0;
+            row[j] = allowed(J, p, j) ? exp(row[j] - m) : 0.0;
             denom += row[j];
         }
         for (int j = 0; j < Tk; ++j) row[j] = row[j] / denom;
@@ -107,7 +117,7 @@ static void run_unit(const job_t *J, int b, int h, double *row) {
              * never read, so nothing after position p_i can reach row i (the
              * makarna loop stops at maxKeyPos the same way) */
             for (int j = 0; j < Tk; ++j) {
-                if (J->causal && (long)j > p) continue;
+                if (!allowed(J, p, j)) continue;
                 const double pj = row[j];
                 const double *vj = vg + (size_t)j * d;
                 for (int e = 0; e < d; ++e) o[e] += pj * vj[e];
@@ -132,9 +142,11 @@ static void *worker(void *arg) {
  */
 int oracle_attention(const double *q, const double *k, const double *v, double *out, double *probs,
                      int B, int Hq, int Hkv, int Tq, int Tk, int d, double scale, int causal,
-                     long pos0, int nthreads) {
+                     long pos0, long window, int nthreads) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Tq < 0 || Tk < 0 || d <= 0 || Hq % Hkv != 0) return -1;
     if (causal != 0 && causal != 1) return -1;
+    /* a local window is a restriction of causal attention; key p_i stays visible */
+    if (window < 0 || (window > 0 && !causal)) return -1;
     /* every query row must have at least one allowed key */
     if (causal && Tq > 0 && (pos0 < 0 || pos0 + Tq > Tk)) return -1;
     if (!causal && Tq > 0 && Tk == 0) return -1;
@@ -154,7 +166,7 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
     }
     int rc = 0, started = 0;
     for (int t = 0; t < nthreads; ++t) {
-        job_t J = {q, k, v, out, probs, B, Hq, Hkv, Tq, Tk, d, causal, pos0, scale, nthreads, t};
+        job_t J = {q, k, v, out, probs, B, Hq, Hkv, Tq, Tk, d, causal, pos0, window, scale, nthreads, t};
         jobs[t] = J;
         if (pthread_create(&th[t], NULL, worker, &jobs[t]) != 0) {
             rc = -2;
