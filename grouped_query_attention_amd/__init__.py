@@ -23,9 +23,10 @@ GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_EHIP = 0, -1, -2, -3, 
 GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
 
 # every symbol include/gqa_attn.h declares
-EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_decode_workspace_bytes",
-            "attn_decode_num_splits", "attn_decode_cached", "attn_decode_paged_workspace_bytes",
-            "attn_decode_paged", "attn_strerror")
+EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_prefill_window", "attn_decode_workspace_bytes",
+            "attn_decode_num_splits", "attn_decode_cached", "attn_decode_window_workspace_bytes",
+            "attn_decode_window", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
+            "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgqa_attn.so is not built (%s); run python grouped_query_attention_amd/build.py"
@@ -48,6 +49,17 @@ lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i
 lib.attn_decode_paged.restype = _i
 lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                   _vp, _sz, _vp]
+lib.attn_prefill_window.restype = _i
+lib.attn_prefill_window.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+lib.attn_decode_window_workspace_bytes.restype = _sz
+lib.attn_decode_window_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+lib.attn_decode_window.restype = _i
+lib.attn_decode_window.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+lib.attn_decode_paged_window_workspace_bytes.restype = _sz
+lib.attn_decode_paged_window_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _i]
+lib.attn_decode_paged_window.restype = _i
+lib.attn_decode_paged_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                         _i, _i, _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
@@ -84,9 +96,11 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def attn_prefill(q, k, v, scale=None, causal=True, out=None, algo=GQA_ALGO_AUTO, stream=None):
+def attn_prefill(q, k, v, scale=None, causal=True, out=None, algo=GQA_ALGO_AUTO, stream=None,
+                 window=None):
     """Causal (or full) GQA prefill.  q [B,Hq,T,d]; k, v [B,Hkv,T,d] (same dtype,
-    float32 or bfloat16).  Returns out [B,Hq,T,d] float32 (written into `out` if given)."""
+    float32 or bfloat16).  Returns out [B,Hq,T,d] float32 (written into `out` if given).
+    window=W (causal only) calls attn_prefill_window: row i sees keys i-W+1 .. i."""
     B, Hq, T, d = q.shape
     if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d or v.shape != k.shape:
         raise ValueError("k, v must be [B, Hkv, T, d] matching q %s; got %s %s"
@@ -100,6 +114,15 @@ def attn_prefill(q, k, v, scale=None, causal=True, out=None, algo=GQA_ALGO_AUTO,
         out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
+    if window is not None:
+        if not causal or algo != GQA_ALGO_AUTO:
+            raise ValueError("a local window needs causal=True and the automatic kernel choice")
+        rc = lib.attn_prefill_window(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                     _dev_ptr(out, "out"), B, Hq, Hkv, T, d, float(scale), int(window),
+                                     _dtype_code(q), _stream_handle(stream, q.device))
+        if rc != GQA_OK:
+            raise GQAError(rc, "attn_prefill_window")
+        return out
     rc = lib.attn_prefill_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
                              B, Hq, Hkv, T, d, float(scale), int(bool(causal)), _dtype_code(q), int(algo),
                              _stream_handle(stream, q.device))
@@ -116,11 +139,18 @@ def attn_decode_num_splits(B, new_tokens, total_len, Hq, Hkv, d, dtype=GQA_BF16)
     return int(lib.attn_decode_num_splits(B, new_tokens, total_len, Hq, Hkv, d, int(dtype)))
 
 
-def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, stream=None):
+def attn_decode_window_workspace_bytes(B, new_tokens, total_len, Hq, Hkv, d, window,
+                                       dtype=GQA_BF16) -> int:
+    return int(lib.attn_decode_window_workspace_bytes(B, new_tokens, total_len, Hq, Hkv, d, int(window),
+                                                      int(dtype)))
+
+
+def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, stream=None, window=None):
     """Cached decode.  q [B,n,Hq,d] (new tokens, token-major); kcache, vcache
     [B,Hkv,L,d] holding positions 0..L-1 with the new tokens at start_pos..start_pos+n-1.
     Scale is 1/sqrt(d).  Returns out [B,n,Hq,d] float32.  A workspace tensor of at least
-    attn_decode_workspace_bytes(...) bytes is allocated here when not supplied."""
+    attn_decode_workspace_bytes(...) bytes is allocated here when not supplied.  window=W
+    keeps new token i's keys start_pos+i-W+1 .. start_pos+i only (attn_decode_window)."""
     B, n, Hq, d = q.shape
     if kcache.dim() != 4 or kcache.shape[0] != B or kcache.shape[3] != d or vcache.shape != kcache.shape:
         raise ValueError("kcache, vcache must be [B, Hkv, L, d]; got %s %s"
@@ -133,16 +163,26 @@ def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, s
         out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
-    need = attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d, dt)
+    if window is None:
+        need = attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d, dt)
+    else:
+        need = attn_decode_window_workspace_bytes(B, n, L, Hq, Hkv, d, window, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.attn_decode_cached(_dev_ptr(q, "q"), _dev_ptr(kcache, "kcache"), _dev_ptr(vcache, "vcache"),
-                                _dev_ptr(out, "out"), n, L, int(start_pos), Hq, Hkv, d, B, dt,
-                                ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if window is None:
+        rc = lib.attn_decode_cached(_dev_ptr(q, "q"), _dev_ptr(kcache, "kcache"), _dev_ptr(vcache, "vcache"),
+                                    _dev_ptr(out, "out"), n, L, int(start_pos), Hq, Hkv, d, B, dt,
+                                    ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+        what = "attn_decode_cached"
+    else:
+        rc = lib.attn_decode_window(_dev_ptr(q, "q"), _dev_ptr(kcache, "kcache"), _dev_ptr(vcache, "vcache"),
+                                    _dev_ptr(out, "out"), n, L, int(start_pos), Hq, Hkv, d, B, int(window),
+                                    dt, ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+        what = "attn_decode_window"
     if rc != GQA_OK:
-        raise GQAError(rc, "attn_decode_cached")
+        raise GQAError(rc, what)
     return out
 
 
@@ -152,12 +192,19 @@ def attn_decode_paged_workspace_bytes(B, new_tokens, Hq, Hkv, d, block_size, max
                                                      max_blocks, int(dtype)))
 
 
+def attn_decode_paged_window_workspace_bytes(B, new_tokens, Hq, Hkv, d, block_size, max_blocks, window,
+                                             dtype=GQA_BF16) -> int:
+    return int(lib.attn_decode_paged_window_workspace_bytes(B, new_tokens, Hq, Hkv, d, block_size,
+                                                            max_blocks, int(window), int(dtype)))
+
+
 def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspace=None,
-                      stream=None):
+                      stream=None, window=None):
     """Paged cached decode.  q [B,n,Hq,d] bf16; kpool, vpool [num_blocks,Hkv,block_size,d]
     bf16; block_table [B,max_blocks] int32 and seq_lens [B] int32 on the GPU (sequence b's
     history of seq_lens[b] positions, new tokens last, lives in the blocks its table row
-    names in order).  Scale is 1/sqrt(d).  Returns out [B,n,Hq,d] float32."""
+    names in order).  Scale is 1/sqrt(d).  window=W keeps each new token's last W positions
+    only (attn_decode_paged_window).  Returns out [B,n,Hq,d] float32."""
     B, n, Hq, d = q.shape
     if kpool.dim() != 4 or kpool.shape[3] != d or vpool.shape != kpool.shape:
         raise ValueError("kpool, vpool must be [num_blocks, Hkv, block_size, d]; got %s %s"
@@ -176,15 +223,24 @@ def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspac
         out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
-    need = attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, dt)
+    if window is None:
+        need = attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, dt)
+    else:
+        need = attn_decode_paged_window_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, window, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.attn_decode_paged(_dev_ptr(q, "q"), _dev_ptr(kpool, "kpool"), _dev_ptr(vpool, "vpool"),
-                               _dev_ptr(block_table, "block_table"), _dev_ptr(seq_lens, "seq_lens"),
-                               _dev_ptr(out, "out"), B, n, Hq, Hkv, d, bs, max_blocks, num_blocks, dt,
-                               ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    ptrs = (_dev_ptr(q, "q"), _dev_ptr(kpool, "kpool"), _dev_ptr(vpool, "vpool"),
+            _dev_ptr(block_table, "block_table"), _dev_ptr(seq_lens, "seq_lens"), _dev_ptr(out, "out"))
+    if window is None:
+        rc = lib.attn_decode_paged(*ptrs, B, n, Hq, Hkv, d, bs, max_blocks, num_blocks, dt,
+                                   ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+        what = "attn_decode_paged"
+    else:
+        rc = lib.attn_decode_paged_window(*ptrs, B, n, Hq, Hkv, d, bs, max_blocks, num_blocks, int(window), dt,
+                                          ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+        what = "attn_decode_paged_window"
     if rc != GQA_OK:
-        raise GQAError(rc, "attn_decode_paged")
+        raise GQAError(rc, what)
     return out

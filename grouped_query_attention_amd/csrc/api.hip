@@ -28,10 +28,12 @@ int check_common(int dtype, int B, int Hq, int Hkv, int d_h) {
 int status_of(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_EHIP; }
 
 int prefill_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
-                 int T, int d_h, float scale, int causal, int dtype, int algo, void* stream) {
+                 int T, int d_h, float scale, int causal, int window, int dtype, int algo,
+                 void* stream) {
   int rc = check_common(dtype, B, Hq, Hkv, d_h);
   if (rc != GQA_OK) return rc;
   if (T < 0 || !isfinite(scale) || (causal != 0 && causal != 1)) return GQA_EINVAL;
+  if (window < 0 || (window > 0 && !causal)) return GQA_EINVAL;
   if (algo != GQA_ALGO_AUTO && algo != GQA_ALGO_GENERIC && algo != GQA_ALGO_MFMA) return GQA_EINVAL;
   if (T > kMaxSeq) return GQA_EUNSUPPORTED;
   // an explicit kernel request is checked even for empty tensors, so a zero-size call
@@ -43,12 +45,12 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (algo == GQA_ALGO_MFMA || (algo == GQA_ALGO_AUTO && mfma_ok)) {
-    gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal};
+    gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window};
     return status_of(gqa::launch_attn_prefill_mfma(a, s));
   }
   const long long sd = d_h;
   gqa::GenericArgs a{q, k, v, out, dtype, B, Hq, Hkv, T, T, d_h, scale, causal, 0,
-                     (long long)Hq * T * sd, (long long)T * sd, sd};
+                     (long long)Hq * T * sd, (long long)T * sd, sd, window};
   return status_of(gqa::launch_attn_generic(a, s));
 }
 
@@ -80,29 +82,109 @@ int decode_check(int newTokens, int totalLen, int startPos, int Hq, int Hkv, int
   return GQA_OK;
 }
 
+size_t decode_ws_impl(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
+                             int window, int dtype) {
+  if (decode_check(newTokens, totalLen, totalLen - newTokens, Hq, Hkv, d_h, B, dtype) != GQA_OK)
+    return 0;
+  if (window < 0 || B == 0 || newTokens == 0) return 0;
+  return gqa::plan_decode(B, newTokens, gqa::decode_key_span(totalLen, newTokens, window), Hq, Hkv,
+                          d_h, dtype)
+      .workspace;
+}
+
+int decode_impl(const void* q, const void* kcache, const void* vcache, float* out,
+                       int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
+                       int window, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = decode_check(newTokens, totalLen, startPos, Hq, Hkv, d_h, B, dtype);
+  if (rc != GQA_OK) return rc;
+  if (window < 0) return GQA_EINVAL;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return GQA_EINVAL;
+  const gqa::DecodePlan plan = gqa::plan_decode(
+      B, newTokens, gqa::decode_key_span(totalLen, newTokens, window), Hq, Hkv, d_h, dtype);
+  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+    return GQA_EWORKSPACE;
+  if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = 1.0f / sqrtf((float)d_h);
+  if (plan.mfma) {
+    gqa::DecodeArgs a{q, kcache, vcache, out, B, newTokens, Hq, Hkv, totalLen, d_h, startPos,
+                      scale, workspace, window};
+    return status_of(gqa::launch_attn_decode_mfma(a, plan, s));
+  }
+  const long long sd = d_h;
+  gqa::GenericArgs a{q, kcache, vcache, out, dtype, B, Hq, Hkv, newTokens, totalLen, d_h, scale,
+                     1, startPos, (long long)newTokens * Hq * sd, sd, (long long)Hq * sd, window};
+  return status_of(gqa::launch_attn_generic(a, s));
+}
+
+size_t paged_ws_impl(int B, int newTokens, int Hq, int Hkv, int d_h, int block_size,
+                            int max_blocks, int window, int dtype) {
+  if (paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, 1, dtype) != GQA_OK)
+    return 0;
+  if (window < 0 || B == 0 || newTokens == 0) return 0;
+  return gqa::plan_decode(B, newTokens,
+                          gqa::decode_key_span(block_size * max_blocks, newTokens, window), Hq,
+                          Hkv, d_h, dtype)
+      .workspace;
+}
+
+int paged_impl(const void* q, const void* kpool, const void* vpool,
+                      const int* block_table, const int* seq_lens, float* out, int B,
+                      int newTokens, int Hq, int Hkv, int d_h, int block_size, int max_blocks,
+                      int num_blocks, int window, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, num_blocks, dtype);
+  if (rc != GQA_OK) return rc;
+  if (window < 0) return GQA_EINVAL;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(kpool) || !aligned16(vpool) || !aligned16(out) ||
+      !aligned4(block_table) || !aligned4(seq_lens))
+    return GQA_EINVAL;
+  const int max_len = block_size * max_blocks;
+  const gqa::DecodePlan plan = gqa::plan_decode(
+      B, newTokens, gqa::decode_key_span(max_len, newTokens, window), Hq, Hkv, d_h, dtype);
+  if (!plan.mfma) return GQA_EUNSUPPORTED;
+  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+    return GQA_EWORKSPACE;
+  if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
+  gqa::DecodeArgs a{q, kpool, vpool, out, B, newTokens, Hq, Hkv, max_len, d_h, 0,
+                    1.0f / sqrtf((float)d_h), workspace, window};
+  gqa::PagedArgs pg{block_table, seq_lens, block_size, max_blocks, num_blocks};
+  return status_of(gqa::launch_attn_decode_paged(a, pg, plan, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
 
 int attn_prefill(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                  int T, int d_h, float scale, int causal, int dtype, void* stream) {
-  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, dtype, GQA_ALGO_AUTO,
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, 0, dtype, GQA_ALGO_AUTO,
                       stream);
 }
 
 int attn_prefill_ex(const void* q, const void* k, const void* v, float* out, int B, int Hq,
                     int Hkv, int T, int d_h, float scale, int causal, int dtype, int algo,
                     void* stream) {
-  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, dtype, algo, stream);
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, 0, dtype, algo, stream);
+}
+
+int attn_prefill_window(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                        int Hkv, int T, int d_h, float scale, int window, int dtype, void* stream) {
+  if (window < 1) return GQA_EINVAL;
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, 1, window, dtype, GQA_ALGO_AUTO,
+                      stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
                                    int dtype) {
-  if (decode_check(newTokens, totalLen, totalLen - newTokens, Hq, Hkv, d_h, B, dtype) != GQA_OK)
-    return 0;
-  if (B == 0 || newTokens == 0) return 0;
-  return gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype).workspace;
+  return decode_ws_impl(B, newTokens, totalLen, Hq, Hkv, d_h, 0, dtype);
 }
+
 
 int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
                            int dtype) {
@@ -112,60 +194,61 @@ int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, 
   return gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype).nsplit;
 }
 
+
 int attn_decode_cached(const void* q, const void* kcache, const void* vcache, float* out,
                        int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = decode_check(newTokens, totalLen, startPos, Hq, Hkv, d_h, B, dtype);
-  if (rc != GQA_OK) return rc;
-  if (B == 0 || newTokens == 0) return GQA_OK;
-  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
-    return GQA_EINVAL;
-  const gqa::DecodePlan plan = gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype);
-  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
-    return GQA_EWORKSPACE;
-  if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const float scale = 1.0f / sqrtf((float)d_h);
-  if (plan.mfma) {
-    gqa::DecodeArgs a{q, kcache, vcache, out, B, newTokens, Hq, Hkv, totalLen, d_h, startPos,
-                      scale, workspace};
-    return status_of(gqa::launch_attn_decode_mfma(a, plan, s));
-  }
-  const long long sd = d_h;
-  gqa::GenericArgs a{q, kcache, vcache, out, dtype, B, Hq, Hkv, newTokens, totalLen, d_h, scale,
-                     1, startPos, (long long)newTokens * Hq * sd, sd, (long long)Hq * sd};
-  return status_of(gqa::launch_attn_generic(a, s));
+  return decode_impl(q, kcache, vcache, out, newTokens, totalLen, startPos, Hq, Hkv, d_h, B, 0,
+                     dtype, workspace, workspace_bytes, stream);
 }
+
+size_t attn_decode_window_workspace_bytes(int B, int newTokens, int totalLen, int Hq, int Hkv,
+                                          int d_h, int window, int dtype) {
+  if (window < 1) return 0;
+  return decode_ws_impl(B, newTokens, totalLen, Hq, Hkv, d_h, window, dtype);
+}
+
+int attn_decode_window(const void* q, const void* kcache, const void* vcache, float* out,
+                       int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
+                       int window, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (window < 1) return GQA_EINVAL;
+  return decode_impl(q, kcache, vcache, out, newTokens, totalLen, startPos, Hq, Hkv, d_h, B, window,
+                     dtype, workspace, workspace_bytes, stream);
+}
+
 
 size_t attn_decode_paged_workspace_bytes(int B, int newTokens, int Hq, int Hkv, int d_h,
                                          int block_size, int max_blocks, int dtype) {
-  if (paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, 1, dtype) != GQA_OK)
-    return 0;
-  if (B == 0 || newTokens == 0) return 0;
-  return gqa::plan_decode(B, newTokens, block_size * max_blocks, Hq, Hkv, d_h, dtype).workspace;
+  return paged_ws_impl(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, 0, dtype);
 }
+
+size_t attn_decode_paged_window_workspace_bytes(int B, int newTokens, int Hq, int Hkv, int d_h,
+                                                int block_size, int max_blocks, int window,
+                                                int dtype) {
+  if (window < 1) return 0;
+  return paged_ws_impl(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, window, dtype);
+}
+
 
 int attn_decode_paged(const void* q, const void* kpool, const void* vpool, const int* block_table,
                       const int* seq_lens, float* out, int B, int newTokens, int Hq, int Hkv,
                       int d_h, int block_size, int max_blocks, int num_blocks, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, num_blocks, dtype);
-  if (rc != GQA_OK) return rc;
-  if (B == 0 || newTokens == 0) return GQA_OK;
-  if (!aligned16(q) || !aligned16(kpool) || !aligned16(vpool) || !aligned16(out) ||
-      !aligned4(block_table) || !aligned4(seq_lens))
-    return GQA_EINVAL;
-  const int max_len = block_size * max_blocks;
-  const gqa::DecodePlan plan = gqa::plan_decode(B, newTokens, max_len, Hq, Hkv, d_h, dtype);
-  if (!plan.mfma) return GQA_EUNSUPPORTED;
-  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
-    return GQA_EWORKSPACE;
-  if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
-  gqa::DecodeArgs a{q, kpool, vpool, out, B, newTokens, Hq, Hkv, max_len, d_h, 0,
-                    1.0f / sqrtf((float)d_h), workspace};
-  gqa::PagedArgs pg{block_table, seq_lens, block_size, max_blocks, num_blocks};
-  return status_of(gqa::launch_attn_decode_paged(a, pg, plan, static_cast<hipStream_t>(stream)));
+  return paged_impl(q, kpool, vpool, block_table, seq_lens, out, B, newTokens, Hq, Hkv, d_h,
+                    block_size, max_blocks, num_blocks, 0, dtype, workspace, workspace_bytes,
+                    stream);
+}
+
+int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool,
+                             const int* block_table, const int* seq_lens, float* out, int B,
+                             int newTokens, int Hq, int Hkv, int d_h, int block_size,
+                             int max_blocks, int num_blocks, int window, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 1) return GQA_EINVAL;
+  return paged_impl(q, kpool, vpool, block_table, seq_lens, out, B, newTokens, Hq, Hkv, d_h,
+                    block_size, max_blocks, num_blocks, window, dtype, workspace, workspace_bytes,
+                    stream);
 }
 
 const char* attn_strerror(int code) {

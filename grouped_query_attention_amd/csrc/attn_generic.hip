@@ -4,7 +4,8 @@
 // that is not a multiple of 16, and odd shapes.  One kernel serves both modes:
 // query row i sits at absolute position pos0 + i (0 for prefill, startPos for
 // cached decode) and sees keys j <= pos0 + i when causal, the key limit of
-// makarna's CausalAttentionCached.
+// makarna's CausalAttentionCached; with a local window W it also needs
+// j >= pos0 + i - W + 1 (the multi-query primer's local attention, section 4.1).
 //
 // Work split: a 256-thread block owns 32 query rows of one query head; each row
 // is served by 8 lanes, each lane holding DPL of the head dims (dims c, c+8,
@@ -32,7 +33,7 @@ template <typename T, int DPL>
 __global__ __launch_bounds__(256) void attn_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ out, int Hq, int Hkv, int Tq, int Tk, int d, float scale_log2, int causal,
-    int pos0, long long q_sb, long long q_sh, long long q_st) {
+    int pos0, int window, long long q_sb, long long q_sh, long long q_st) {
   constexpr int DP = DPL * kLanesPerRow;  // padded head dim held by one row
   __shared__ float Ks[kKeysPerTile * DP];
   __shared__ float Vs[kKeysPerTile * DP];
@@ -61,12 +62,15 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
   }
   float m = -INFINITY, l = 0.f;
 
-  // Keys this block can need: all of them, or up to the last row's position.
+  // Keys this block can need: all of them, or up to the last row's position, and with
+  // a window from the first row's window start.
   const int last_row = min(Tq, row0 + kRowsPerBlock) - 1;
   const long long lim_ll = causal ? min((long long)Tk, (long long)pos0 + last_row + 1) : (long long)Tk;
   const int kv_lim = (int)lim_ll;
+  const int kv_beg = window > 0 ? (int)max(0LL, (long long)pos0 + row0 - window + 1) : 0;
+  const long long lo = pos - window + 1;  // this row's first visible key (window > 0)
 
-  for (int j0 = 0; j0 < kv_lim; j0 += kKeysPerTile) {
+  for (int j0 = kv_beg; j0 < kv_lim; j0 += kKeysPerTile) {
     __syncthreads();
     for (int idx = tid; idx < kKeysPerTile * DP; idx += 256) {
       const int jj = idx / DP, e = idx % DP;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
       part += __shfl_xor(part, 2);
       part += __shfl_xor(part, 4);
       const int j = j0 + jj;
-      const bool allowed = j < kv_lim && (!causal || (long long)j <= pos);
+      const bool allowed = j < kv_lim && (!causal || (long long)j <= pos) && (window <= 0 || j >= lo);
       s[jj] = allowed ? part : -INFINITY;
       tmax = fmaxf(tmax, s[jj]);
     }
@@ -126,7 +130,8 @@ hipError_t launch_t(const GenericArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_generic_kernel<T, DPL>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.out, a.Hq, a.Hkv, a.Tq, a.Tk, a.d,
-                     a.scale * 1.4426950408889634f, a.causal, a.pos0, a.q_sb, a.q_sh, a.q_st);
+                     a.scale * 1.4426950408889634f, a.causal, a.pos0, a.window, a.q_sb, a.q_sh,
+                     a.q_st);
   return hipGetLastError();
 }
 

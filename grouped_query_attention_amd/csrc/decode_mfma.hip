@@ -66,7 +66,16 @@ struct KvSource {
   int L;             // contiguous: rows per head in the cache
   int start_pos;     // contiguous: position of the first new token (every sequence)
   int bs, max_blocks, num_blocks, max_len;  // paged
+  int window;        // local window (keys p-W+1 .. p); 0 = none
 };
+
+// First key the kernels walk: the first new token's window start, rounded down to the
+// 32-key tile (so 16-row groups stay inside 16-aligned blocks); 0 without a window.
+__host__ __device__ __forceinline__ int key_begin(int kv_len, int n, int window) {
+  if (window <= 0) return 0;
+  const int lo = kv_len - n - window + 1;
+  return lo <= 0 ? 0 : (lo / kTile) * kTile;
+}
 
 __device__ __forceinline__ float xmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
@@ -111,7 +120,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
   }
   const int start_pos = kv_len - n;
   const int last = kv_len - 1;  // rows past it are never read
-  const int c0 = split * chunk;
+  const int kbeg = key_begin(kv_len, n, kv.window);
+  const int c0 = kbeg + split * chunk;
   if (c0 >= kv_len) return;  // empty chunk: the merge only reads chunks below kv_len
   const int c1 = min(c0 + chunk, kv_len);
 
@@ -122,6 +132,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
   const int tok = col_ok ? cidx / G : 0;  // columns are token-major: (token, head in group)
   const int hq = g * G + (col_ok ? cidx % G : 0);
   const int qpos = start_pos + tok;  // absolute position of the column's token
+  const int qlo = kv.window > 0 ? qpos - kv.window + 1 : 0;  // its first visible key
 
   // Q^T fragments: column cidx, head dims 32*st + 8*grp + 0..7 (zero past D)
   bf16x8 qf[G_::kSteps];
@@ -248,14 +259,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
       for (int st = 0; st < G_::kSteps; ++st)
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][st], qf[st], s[kb], 0, 0, 0);
     }
-    // keys past the chunk, or after the column's own position, get no weight
-    if (j0 + kTile > c1 || j0 + kTile - 1 > start_pos) {
+    // keys past the chunk, after the column's own position, or below its window get
+    // no weight
+    if (j0 + kTile > c1 || j0 + kTile - 1 > start_pos || (kv.window > 0 && j0 < kv_len - kv.window)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = j0 + 16 * kb + 4 * grp + r;
-          if (j >= c1 || j > qpos) s[kb][r] = -INFINITY;
+          if (j >= c1 || j > qpos || j < qlo) s[kb][r] = -INFINITY;
         }
     }
     float mx = xmax(xmax(xmax(s[0][0], s[0][1]), xmax(s[0][2], s[0][3])),
@@ -357,7 +369,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   } else {
     kv_len = kv.start_pos + n;
   }
-  const int nvalid = (kv_len + chunk - 1) / chunk;
+  const int nvalid = (kv_len - key_begin(kv_len, n, kv.window) + chunk - 1) / chunk;
   const long long base = (long long)bg * nsplit * ncols + cidx;  // partial index of split 0
 
   float M = -INFINITY;
@@ -424,9 +436,16 @@ hipError_t launch_any_d(const DecodeArgs& a, const KvSource& kv, const DecodePla
 
 }  // namespace
 
+int decode_key_span(int len, int n, int window) {
+  if (window <= 0) return len;
+  // the widest case: key_begin rounds the window start down by up to kTile - 1 keys
+  const long long span = (long long)window + n - 1 + (kTile - 1);
+  return span < len ? (int)span : len;
+}
+
 // Pure function of the shape: enough chunks that the launch has ~kTargetWaves waves,
 // each chunk a multiple of the 32-key tile; partials are (d + 2) floats per chunk,
-// query row and head.
+// query row and head.  `total_len` is the most keys one sequence walks.
 DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int dtype) {
   DecodePlan p{1, total_len, 0, false};
   p.mfma = dtype == kBF16 && d % 16 == 0 && d <= 128 && total_len > 0;
@@ -447,7 +466,7 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
 
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), nullptr,
-              nullptr, a.L, a.start_pos, 0, 0, 0, 0};
+              nullptr, a.L, a.start_pos, 0, 0, 0, 0, a.window};
   return launch_any_d<false>(a, kv, p, stream);
 }
 
@@ -455,7 +474,7 @@ hipError_t launch_attn_decode_paged(const DecodeArgs& a, const PagedArgs& pg, co
                                     hipStream_t stream) {
   KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), pg.table,
               pg.seq_lens, 0, 0, pg.block_size, pg.max_blocks, pg.num_blocks,
-              pg.block_size * pg.max_blocks};
+              pg.block_size * pg.max_blocks, a.window};
   return launch_any_d<true>(a, kv, p, stream);
 }
 

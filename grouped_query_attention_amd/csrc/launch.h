@@ -24,6 +24,7 @@ struct GenericArgs {
   int causal;
   int pos0;
   long long q_sb, q_sh, q_st;  // strides of q and out: batch, head, row
+  int window;                  // local window (causal only); 0 = none
 };
 hipError_t launch_attn_generic(const GenericArgs& a, hipStream_t stream);
 
@@ -36,6 +37,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, T, d;
   float scale;
   int causal;
+  int window;  // local window (causal only); 0 = none
 };
 bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
@@ -47,7 +49,13 @@ struct DecodePlan {
   size_t workspace;  // bytes of partial results
   bool mfma;         // the bf16 matrix-core decode kernel applies
 };
-DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int dtype);
+// `span` is the most keys one sequence's new tokens can see: the history length, or
+// with a local window W at most W + n - 1 (+ alignment, see decode_key_span).
+DecodePlan plan_decode(int B, int n, int span, int Hq, int Hkv, int d, int dtype);
+// Keys the split kernel walks for a history of `len` positions with n new tokens and
+// local window `window` (0 = none): the window's first key rounded down to the
+// 32-key tile, up to len.  The host bound for paged decode uses len = max_len.
+int decode_key_span(int len, int n, int window);
 
 struct DecodeArgs {
   const void* q;   // [B, n, Hq, d]
@@ -57,6 +65,7 @@ struct DecodeArgs {
   int B, n, Hq, Hkv, L, d, start_pos;
   float scale;
   void* workspace;
+  int window;      // local window; 0 = none
 };
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
 

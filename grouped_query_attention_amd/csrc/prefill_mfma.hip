@@ -27,7 +27,10 @@
 //    staging) in stages of 128 keys, double-buffered in two separate LDS arrays; the
 //    next stage's loads are issued once the current stage's last LDS reads are out.
 //  * Causal skipping: 64-key tiles entirely above a wave's diagonal are not computed;
-//    the mask is only evaluated on diagonal tiles.
+//    the mask is only evaluated on diagonal tiles.  A local window (the multi-query
+//    primer's local attention, section 4.1: keys p-W+1 .. p) skips from both sides:
+//    stages below the workgroup's first window start are never loaded, tiles below a
+//    wave's window are not computed, and window-edge tiles are masked.
 //  * Heaviest q-tiles are dispatched first; blocks of one (batch, head group) keep
 //    the same block-id residue mod 8, i.e. stay on one XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -87,7 +90,7 @@ template <int D, int HPW>
 __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int Hq, int Hkv, int T, float c,
-    unsigned qsign, int causal, int n_qtiles, int n_hgroups, int B) {
+    unsigned qsign, int causal, int window, int n_qtiles, int n_hgroups, int B) {
   using G_ = Geo<D>;
   constexpr int NT = kWgWaves * 64;
   constexpr int SLICES = kWgWaves / HPW;  // 32-row slices per head
@@ -143,6 +146,8 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
 
   const int kend = causal ? min(T, q0 + QT) : T;
   const int nstages = (kend + kStage - 1) / kStage;
+  // a local window (causal only) also drops the stages below the first row's window
+  const int t0 = window > 0 ? max(0, q0 - window + 1) / kStage : 0;
 
   // Tile staging with direct global->LDS loads (global_load_lds_dwordx4, no register
   // staging): one wave instruction writes 64 consecutive 16-byte LDS slots; slot p of a
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
 
   };
   auto part_b = [&](int k0, bool diag, f32x16 (&s)[2], const bf16x8 (&vf)[2][2][G_::kDBlocks]) {
-      // mask (diagonal tiles only): key j of accumulator r is
+      // mask (diagonal and window-edge tiles only): key j of accumulator r is
       // k0 + 32*sb + 8*(r/4) + 4*half + r%4
       if (diag) {
 #pragma unroll
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = causal ? (j <= qi) : (j < T);
+            const bool ok = causal ? (j <= qi && (window <= 0 || j > qi - window)) : (j < T);
             if (!ok) s[sb][r] = -INFINITY;
           }
       }
@@ -280,7 +285,10 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       }
 
       // p = 2^(s*c - m), rounded to bf16 for the P V product; the normalizer sums the
-      // same bf16 values, two per v_dot2_f32_bf16 against (1, 1)
+      // same bf16 values, two per v_dot2_f32_bf16 against (1, 1).  Under a window a
+      // column can meet a tile entirely below its window before any visible key
+      // (m = -inf): 0 is then the reference, and its p are exact zeros.
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
       bf16x8 pb[2][2];
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float lsum[2] = {0.f, 0.f};
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pb[sb][kk][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][8 * kk + e], c, -m_run));
+            pb[sb][kk][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][8 * kk + e], c, -m_ref));
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             const bf16x2 pr = {pb[sb][kk][e], pb[sb][kk][e + 1]};
@@ -318,9 +326,13 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int sub = 0; sub < kSub; ++sub) {
       const int k0 = t * kStage + sub * kBN;
-      // keys k0.. are all beyond this wave's last row, or past T: nothing to do
-      const bool active = (!causal || k0 <= qw + 31) && k0 < T;
-      const bool diag = causal ? (k0 + kBN - 1 > qw) : (k0 + kBN > T);
+      // keys k0.. are all beyond this wave's last row, past T, or below the window of
+      // its first row: nothing to do.  The mask is needed where some key is after
+      // the first row or below the last row's window.
+      const bool active = (!causal || k0 <= qw + 31) && k0 < T &&
+                          (window <= 0 || k0 + kBN - 1 > qw - window);
+      const bool diag = causal ? (k0 + kBN - 1 > qw || (window > 0 && k0 <= qw + 31 - window))
+                               : (k0 + kBN > T);
       f32x16 s[2];
       bf16x8 vf[2][2][G_::kDBlocks];
       if (active) part_a(k0, cur + sub * kBN * G_::kKStride, cur + G_::kKTile + sub * kBN * G_::kVStride, s, vf);
@@ -334,10 +346,10 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     __syncthreads();
   };
 
-  stage(0, lds_a);
+  stage(t0, lds_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < nstages; t += 2) {
+  for (int t = t0; t < nstages; t += 2) {
     step(t, lds_a, lds_b);
     if (t + 1 < nstages) step(t + 1, lds_b, lds_a);
   }
@@ -376,7 +388,7 @@ hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW>), dim3((unsigned)nblocks), dim3(kWgWaves * 64), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, a.Hq, a.Hkv, a.T, c, qsign, a.causal,
-                     n_qtiles, n_hgroups, a.B);
+                     a.causal ? a.window : 0, n_qtiles, n_hgroups, a.B);
   return hipGetLastError();
 }
 

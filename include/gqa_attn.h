@@ -78,6 +78,16 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, float* out, int
                     void* stream);
 
 /*
+ * Local (sliding-window) causal prefill: as attn_prefill with causal = 1, except that
+ * query row i sees only keys max(0, i - window + 1) .. i (the multi-query primer's
+ * local attention, section 4.1: the current position and the previous window-1).
+ * window >= T gives plain causal attention.  Keys below every row's window are never
+ * read.  Errors as attn_prefill, plus GQA_EINVAL for window < 1.
+ */
+int attn_prefill_window(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                        int Hkv, int T, int d_h, float scale, int window, int dtype, void* stream);
+
+/*
  * Bytes of device workspace attn_decode_cached needs for this shape (0 when it needs
  * none).  Pure host arithmetic; the same arguments always give the same answer.
  * Returns 0 for arguments attn_decode_cached would reject.
@@ -114,6 +124,22 @@ int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, 
 int attn_decode_cached(const void* q, const void* kcache, const void* vcache, float* out,
                        int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Local-window cached decode: attn_decode_cached where new token i (position
+ * startPos + i) sees only keys startPos + i - window + 1 .. startPos + i.  Only the cache
+ * rows from the first new token's window start (rounded down to a multiple of 32) up
+ * to startPos + newTokens - 1 are read, and the key split is planned for that span, so
+ * the cost follows the window, not the history.  Arguments and errors as
+ * attn_decode_cached, plus GQA_EINVAL for window < 1; the workspace is
+ * attn_decode_window_workspace_bytes(...) (0 for window < 1 or rejected shapes).
+ */
+size_t attn_decode_window_workspace_bytes(int B, int newTokens, int totalLen, int Hq, int Hkv,
+                                          int d_h, int window, int dtype);
+int attn_decode_window(const void* q, const void* kcache, const void* vcache, float* out,
+                       int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
+                       int window, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * Bytes of device workspace attn_decode_paged needs (0 when it needs none).  The key
@@ -159,6 +185,24 @@ int attn_decode_paged(const void* q, const void* kpool, const void* vpool,
                       int newTokens, int Hq, int Hkv, int d_h, int block_size, int max_blocks,
                       int num_blocks, int dtype, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * Local-window paged decode: attn_decode_paged where new token i of sequence b
+ * (position seq_lens[b] - newTokens + i) sees only the last `window` positions up to
+ * its own.  Table entries of blocks that lie entirely below the first new token's
+ * window start (rounded down to a multiple of 32) are never read, so a sliding-window
+ * cache may already have released them.  Arguments and errors as attn_decode_paged,
+ * plus GQA_EINVAL for window < 1; the workspace is
+ * attn_decode_paged_window_workspace_bytes(...).
+ */
+size_t attn_decode_paged_window_workspace_bytes(int B, int newTokens, int Hq, int Hkv, int d_h,
+                                                int block_size, int max_blocks, int window,
+                                                int dtype);
+int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool,
+                             const int* block_table, const int* seq_lens, float* out, int B,
+                             int newTokens, int Hq, int Hkv, int d_h, int block_size,
+                             int max_blocks, int num_blocks, int window, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* attn_strerror(int code);

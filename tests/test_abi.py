@@ -184,3 +184,31 @@ def test_paged_workspace_checked_before_launch():
     # rejected shapes need nothing
     assert gqa.attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, 24, mb, BF16) == 0
     assert gqa.attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, mb, F32) == 0
+
+
+def test_window_entry_points_reject_bad_windows():
+    f = ctypes.c_float(0.5)
+    for w in (0, -1):
+        assert lib.attn_prefill_window(A16, A16, A16, A16, 1, 2, 1, 8, 64, f, w, BF16, None) == EINVAL
+        assert lib.attn_decode_window(A16, A16, A16, A16, 1, 16, 15, 4, 1, 64, 1, w, BF16, A16, 1 << 30,
+                                      None) == EINVAL
+        assert lib.attn_decode_paged_window(A16, A16, A16, A16, A16, A16, 2, 1, 4, 1, 64, 16, 8, 16, w,
+                                            BF16, A16, 1 << 30, None) == EINVAL
+        assert gqa.attn_decode_window_workspace_bytes(64, 1, 32768, 32, 8, 128, w) == 0
+        assert gqa.attn_decode_paged_window_workspace_bytes(64, 1, 32, 8, 128, 16, 2048, w) == 0
+    # the other checks still apply
+    assert lib.attn_prefill_window(A16, A16, A16, A16, 1, 3, 2, 8, 64, f, 4, BF16, None) == EINVAL
+    assert lib.attn_prefill_window(None, None, None, None, 0, 2, 1, 8, 64, f, 4, BF16, None) == OK
+
+
+def test_window_workspace_follows_the_window():
+    """The split plan of a window decode covers the window's keys, not the history."""
+    B, n, L, Hq, Hkv, d = 64, 1, 32768, 32, 8, 128
+    full = gqa.attn_decode_workspace_bytes(B, n, L, Hq, Hkv, d)
+    for W in (32, 1000, 4096):
+        w = gqa.attn_decode_window_workspace_bytes(B, n, L, Hq, Hkv, d, W)
+        assert 0 < w <= full
+        p = gqa.attn_decode_paged_window_workspace_bytes(B, n, Hq, Hkv, d, 16, L // 16, W)
+        assert p == w
+    # a window wider than the history plans the history
+    assert gqa.attn_decode_window_workspace_bytes(B, n, L, Hq, Hkv, d, 10 * L) == full
