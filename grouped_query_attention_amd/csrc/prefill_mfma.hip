@@ -86,12 +86,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool WIN>
 __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int Hq, int Hkv, int T, float c,
-    unsigned qsign, int causal, int window, int n_qtiles, int n_hgroups, int B) {
+    unsigned qsign, int causal, int window_arg, int n_qtiles, int n_hgroups, int B) {
   using G_ = Geo<D>;
+  // the local window is a separate instantiation: plain causal attention carries none
+  // of its checks
+  const int window = WIN ? window_arg : 0;
   constexpr int NT = kWgWaves * 64;
   constexpr int SLICES = kWgWaves / HPW;  // 32-row slices per head
   constexpr int QT = 32 * SLICES;         // query rows per head per workgroup
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       // same bf16 values, two per v_dot2_f32_bf16 against (1, 1).  Under a window a
       // column can meet a tile entirely below its window before any visible key
       // (m = -inf): 0 is then the reference, and its p are exact zeros.
-      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+      const float m_ref = (WIN && m_run == -INFINITY) ? 0.f : m_run;
       bf16x8 pb[2][2];
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float lsum[2] = {0.f, 0.f};
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   }
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool WIN>
 hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   constexpr int QT = 32 * (kWgWaves / HPW);
   const int n_qtiles = (a.T + QT - 1) / QT;
@@ -385,7 +388,7 @@ hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   // masked scores at -inf without changing any visible weight measurably
   if (c == 0.f) c = 1e-30f;
   const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW>), dim3((unsigned)nblocks), dim3(kWgWaves * 64), 0,
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW, WIN>), dim3((unsigned)nblocks), dim3(kWgWaves * 64), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, a.Hq, a.Hkv, a.T, c, qsign, a.causal,
                      a.causal ? a.window : 0, n_qtiles, n_hgroups, a.B);
@@ -395,8 +398,9 @@ hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  if (G % 2 == 0) return launch_dh<D, 2>(a, stream);
-  return launch_dh<D, 1>(a, stream);
+  const bool win = a.causal && a.window > 0;
+  if (G % 2 == 0) return win ? launch_dh<D, 2, true>(a, stream) : launch_dh<D, 2, false>(a, stream);
+  return win ? launch_dh<D, 1, true>(a, stream) : launch_dh<D, 1, false>(a, stream);
 }
 
 }  // namespace
