@@ -213,3 +213,16 @@ def paged_from_contiguous(kc, vc, block_size: int, seed: int):
         pools.append(pool)
     lens = torch.full((B,), L, dtype=torch.int32, device=kc.device)
     return pools[0], pools[1], table.to(kc.device), lens
+
+
+def kv_append_inputs(B, n, Hkv, d, L, cache_dtype, seed):
+    """New tokens k_new, v_new [B,n,Hkv,d] float32 (the projections), the caches they go
+    into [B,Hkv,L,d] (N(0,1) history in cache_dtype) and per-pair frequency factors [d/2]
+    drawn uniformly from [1, 4); fill order k_new, v_new, kcache, vcache, factors."""
+    g = torch.Generator().manual_seed(int(seed))
+    k_new = normal((B, n, Hkv, d), g, "f32")
+    v_new = normal((B, n, Hkv, d), g, "f32")
+    kc = normal((B, Hkv, L, d), g, cache_dtype)
+    vc = normal((B, Hkv, L, d), g, cache_dtype)
+    ff = 1.0 + 3.0 * torch.rand(d // 2, generator=g, dtype=torch.float32)
+    return k_new, v_new, kc, vc, ff
