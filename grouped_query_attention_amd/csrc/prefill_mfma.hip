@@ -155,38 +155,42 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   // Tile staging with direct global->LDS loads (global_load_lds_dwordx4, no register
   // staging): one wave instruction writes 64 consecutive 16-byte LDS slots; slot p of a
   // tile is row p / P, chunk p % P of a row padded to P chunks.  A lane's source offset
-  // inside a tile is the same for every tile, so it is computed once here.  Padding
-  // slots re-read chunk 0 of their row.  In a ragged last tile, rows at or past T read
-  // row T-1 instead: those keys are masked, and their finite values meet probability 0.
-  constexpr int KP = G_::kKStride / 16, VP = G_::kVStride / 16, C16 = D / 8;
+  // inside a tile is the same for every tile, so it is computed once here, as one byte
+  // offset per wave instruction.  Padding slots re-read chunk 0 of their row.  In a
+  // ragged last tile, rows at or past T read row T-1 instead: those keys are masked,
+  // and their finite values meet probability 0.
+  constexpr int KP = G_::kKStride / 16, VP = G_::kVStride / 16, C16 = D / 8, RB = D * 2;
   constexpr int KI = (kSub * KP + kWgWaves - 1) / kWgWaves;  // wave instructions per wave per stage
   constexpr int VI = (kSub * VP + kWgWaves - 1) / kWgWaves;
-  int krow[KI], koff[KI], vrow[VI], voff[VI];
+  int koff[KI], voff[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
-    const int p = (wave + kWgWaves * i) * 64 + lane, r = p / KP, cc = p % KP;
-    krow[i] = r;
-    koff[i] = (cc < C16 ? cc : 0) * 16;
+    const int p = (wave + kWgWaves * i) * 64 + lane, cc = p % KP;
+    koff[i] = (p / KP) * RB + (cc < C16 ? cc : 0) * 16;
   }
 #pragma unroll
   for (int i = 0; i < VI; ++i) {
-    const int p = (wave + kWgWaves * i) * 64 + lane, r = p / VP, cc = p % VP;
-    vrow[i] = r;
-    voff[i] = (cc < C16 ? cc : 0) * 16;
+    const int p = (wave + kWgWaves * i) * 64 + lane, cc = p % VP;
+    voff[i] = (p / VP) * RB + (cc < C16 ? cc : 0) * 16;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // clamp a source offset to the last valid row of a ragged stage
+  auto clamp_row = [&](int off, int rmax) {
+    const int r = off / RB;
+    return r > rmax ? off - (r - rmax) * RB : off;
+  };
   auto stage = [&](int t, char* dst) {
-    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kStage * D * 2;
-    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kStage * D * 2;
+    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kStage * RB;
+    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kStage * RB;
     const bool ragged = t * kStage + kStage > T;
     const int rmax = T - 1 - t * kStage;  // last valid row of this stage
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int inst = wave_u + kWgWaves * i;
       if (inst < kSub * KP) {
-        const int r = ragged ? min(krow[i], rmax) : krow[i];
+        const int off = ragged ? clamp_row(koff[i], rmax) : koff[i];
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(kb + r * (D * 2) + koff[i]),
+            (const __attribute__((address_space(1))) void*)(kb + off),
             (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
       }
     }
@@ -194,169 +198,220 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     for (int i = 0; i < VI; ++i) {
       const int inst = wave_u + kWgWaves * i;
       if (inst < kSub * VP) {
-        const int r = ragged ? min(vrow[i], rmax) : vrow[i];
+        const int off = ragged ? clamp_row(voff[i], rmax) : voff[i];
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(vb + r * (D * 2) + voff[i]),
+            (const __attribute__((address_space(1))) void*)(vb + off),
             (__attribute__((address_space(3))) void*)(dst + G_::kKTile + inst * 1024), 16, 0, 0);
       }
     }
   };
 
-  // One compute tile of 64 keys at k0, in two parts: (A) LDS fragment reads and S^T,
-  // (B) mask, softmax and the P V products.
-  auto part_a = [&](int k0, const char* kl, const char* vl, f32x16 (&s)[2],
-                    bf16x8 (&vf)[2][2][G_::kDBlocks]) {
-      // S^T = K Q^T: all K fragments of the tile are read before the matrix ops so
-      // the LDS latency is paid once, and the two 32-key blocks form two
-      // independent accumulation chains.
-      {
-        bf16x8 kf[2][G_::kSteps];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const char* krow = kl + (sb * 32 + col) * G_::kKStride + half * 16;
-#pragma unroll
-          for (int st = 0; st < G_::kSteps; ++st)
-            kf[sb][st] = *reinterpret_cast<const bf16x8*>(krow + st * 32);
-        }
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int st = 0; st < G_::kSteps; ++st) {
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][st], qf[st], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][st], qf[st], s[1], 0, 0, 0);
-        }
-        __builtin_amdgcn_s_setprio(0);
-      }
+  // ---- per-block pieces.  The online softmax runs over 32-key blocks: a block's S^T
+  // is one 32x32 accumulator in which every lane holds 16 keys of its own query.
+  constexpr int KS = G_::kSteps, DB = G_::kDBlocks;
+  constexpr int kBlk = 32;                // keys per softmax block
+  constexpr int kNB = kStage / kBlk;      // blocks per LDS stage
 
-      // V^T fragments for O^T += V^T P^T, issued now so their latency hides under the
-      // softmax.  Transposed-read addressing inside each 16-lane group: lane s reads 4
-      // head dims (m0 + 4*(s%4) ..) of key row (k0p + s/4); after the transpose lane s
-      // holds head dim m0 + s of keys k0p .. k0p+3.
-      {
-        const int grp = lane >> 4, sl = lane & 15;
-        const int voff = (sl >> 2) * G_::kVStride + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+  // K fragments of the block whose first K row is kl: the lane holds key row `col`,
+  // head dims 16*st + 8*half .. +7 (the A operand of S^T = K Q^T)
+  auto read_k = [&](const char* kl, bf16x8 (&kf)[KS]) {
+    const char* krow = kl + col * G_::kKStride + half * 16;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const char* vrow = vl + (32 * sb + 16 * kk + 4 * half) * G_::kVStride + voff;
-#pragma unroll
-            for (int db = 0; db < G_::kDBlocks; ++db) {
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + db * 64));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_i16x4*)(vrow + 8 * G_::kVStride + db * 64));
-              vf[sb][kk][db] = __builtin_bit_cast(
-                  bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-          }
-      }
-
+    for (int st = 0; st < KS; ++st) kf[st] = *reinterpret_cast<const bf16x8*>(krow + st * 32);
   };
-  auto part_b = [&](int k0, bool diag, f32x16 (&s)[2], const bf16x8 (&vf)[2][2][G_::kDBlocks]) {
-      // mask (diagonal and window-edge tiles only): key j of accumulator r is
-      // k0 + 32*sb + 8*(r/4) + 4*half + r%4
-      if (diag) {
+  // V^T fragments of the block whose first V row is vl.  Transposed-read addressing
+  // inside each 16-lane group: lane s reads 4 head dims (m0 + 4*(s%4) ..) of key row
+  // (k0p + s/4); after the transpose lane s holds head dim m0 + s of keys k0p .. k0p+3.
+  auto read_v = [&](const char* vl, bf16x8 (&vf)[2][DB]) {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int voff = (sl >> 2) * G_::kVStride + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+    for (int kk = 0; kk < 2; ++kk) {
+      const char* vrow = vl + (16 * kk + 4 * half) * G_::kVStride + voff;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = causal ? (j <= qi && (window <= 0 || j > qi - window)) : (j < T);
-            if (!ok) s[sb][r] = -INFINITY;
-          }
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + db * 64));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + 8 * G_::kVStride + db * 64));
+        vf[kk][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-
-      // NaN-propagating maximum lowers to v_maximum3_f32 with no operand
-      // canonicalization (fmaxf would add one v_max per score)
-      float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r)
-        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[0][r]), s[1][r]);
-      mx = pair_max(mx);
-      const float mt = mx * c;  // tile max in log2 units
-      const bool need = mt > m_run + kLazyTau;
-      if (__any(need)) {
-        const float m_new = need ? mt : m_run;
-        // lanes that keep their max keep their scale: exp2(m - m) would be NaN
-        // for a column that has seen only masked keys (m = -inf)
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < G_::kDBlocks; ++db) o[db] *= alpha;
-        m_run = m_new;
-      }
-
-      // p = 2^(s*c - m), rounded to bf16 for the P V product; the normalizer sums the
-      // same bf16 values, two per v_dot2_f32_bf16 against (1, 1).  Under a window a
-      // column can meet a tile entirely below its window before any visible key
-      // (m = -inf): 0 is then the reference, and its p are exact zeros.
-      const float m_ref = (WIN && m_run == -INFINITY) ? 0.f : m_run;
-      bf16x8 pb[2][2];
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float lsum[2] = {0.f, 0.f};
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pb[sb][kk][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][8 * kk + e], c, -m_ref));
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pr = {pb[sb][kk][e], pb[sb][kk][e + 1]};
-            lsum[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[kk], false);
-          }
-        }
-      l_part += lsum[0] + lsum[1];
-
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int db = 0; db < G_::kDBlocks; ++db)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][kk][db], pb[sb][kk], o[db], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
+    }
   };
-  // One LDS stage of kSub compute tiles.  The transposed V reads must not meet
-  // direct-to-LDS loads in flight (the compiler cannot tell them apart and would wait
-  // for the loads there), so the next stage's loads are issued after this stage's last
-  // LDS reads, behind a compiler memory barrier, and overlap the last tile's softmax
-  // and P V products.
-  auto step = [&](int t, const char* cur, char* nxt) {
+  // S^T = K Q^T for one block: accumulator r holds key 8*(r/4) + 4*half + r%4 of the
+  // block, for this lane's query
+  auto mfma_s = [&](const bf16x8 (&kf)[KS], f32x16& s) {
+    s = f32x16{};
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) {
-      const int k0 = t * kStage + sub * kBN;
+    for (int st = 0; st < KS; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s, 0, 0, 0);
+  };
+  // O^T += V^T P^T over one block; P's lane order of keys {4h..4h+3, 8+4h..} in each
+  // 16-key step is a valid K-ordering because V^T is read in the same order
+  auto mfma_pv = [&](const bf16x8 (&vf)[2][DB], const bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][db], pb[kk], o[db], 0, 0, 0);
+  };
+  // mask of a diagonal or window-edge block at key k0
+  auto mask_blk = [&](f32x16& s, int k0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const bool ok = causal ? (j <= qi && (window <= 0 || j > qi - window)) : (j < T);
+      if (!ok) s[r] = -INFINITY;
+    }
+  };
+  // Online-softmax step for one block: move the running max lazily (only when it grows
+  // by more than kLazyTau), rescale the normalizer, and form p = 2^(s*c - m) in bf16.
+  // Returns whether any lane moved its max; the numerator must then be scaled by
+  // `alpha` before this block's P V is added.
+  auto softmax_blk = [&](const f32x16& s, bf16x8 (&pb)[2], float& alpha) -> bool {
+    // NaN-propagating maximum lowers to v_maximum3_f32 with no operand
+    // canonicalization (fmaxf would add one v_max per score)
+    float mx = __builtin_elementwise_maximum(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[r]), s[r + 1]);
+    mx = pair_max(mx);
+    const float mt = mx * c;  // block max in log2 units
+    const bool need = mt > m_run + kLazyTau;
+    // lanes that keep their max keep their scale: exp2(m - m) would be NaN for a
+    // column that has seen only masked keys (m = -inf)
+    alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+    m_run = need ? mt : m_run;
+    l_part *= alpha;
+    // p, rounded to bf16 for the P V product; the normalizer sums the same bf16
+    // values, two per v_dot2_f32_bf16 against (1, 1).  Under a window a column can
+    // meet a block entirely below its window before any visible key (m = -inf): 0 is
+    // then the reference, and its p are exact zeros.
+    const float m_ref = (WIN && m_run == -INFINITY) ? 0.f : m_run;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pb[kk][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + e], c, -m_ref));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pb[kk][e], pb[kk][e + 1]};
+        ls[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[kk], false);
+      }
+    }
+    l_part += ls[0] + ls[1];
+    return __any(need);
+  };
+  auto rescale_o = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  };
+
+  // P V of an interior stage's last block, deferred past the stage barrier (its V
+  // fragments are already in registers) so it runs beside the next stage's first S^T.
+  bf16x8 pend_v[2][DB];
+  bf16x8 pend_p[2];
+  bool pending = false;
+
+  // Stage whose blocks are all fully visible to every row of this wave: a software
+  // pipeline over its blocks.  Region b runs the softmax of block b on the vector ALU
+  // beside the S^T of block b+1 and the P V of block b-1 on the matrix core, so the
+  // wave's own instruction stream keeps both busy.
+  auto interior_stage = [&](const char* kl, const char* vl) {
+    f32x16 s[kNB];
+    bf16x8 pb[kNB][2];
+    {
+      bf16x8 kf[KS];
+      read_k(kl, kf);
+      if (pending) mfma_pv(pend_v, pend_p);  // needs no LDS: covers the K read latency
+      mfma_s(kf, s[0]);
+    }
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      bf16x8 kf[KS];
+      bf16x8 vf[2][DB];
+      if (b + 1 < kNB) read_k(kl + (b + 1) * kBlk * G_::kKStride, kf);
+      if (b >= 1) read_v(vl + (b - 1) * kBlk * G_::kVStride, vf);
+      float alpha;
+      const bool resc = softmax_blk(s[b], pb[b], alpha);
+      if (b + 1 < kNB) mfma_s(kf, s[b + 1]);
+      if (b >= 1) mfma_pv(vf, pb[b - 1]);
+      // interleave: K reads, the max (vector ops), then one matrix op per four vector
+      // ops; the V reads go out once the first S^T ops have freed their K registers
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (i >= 3 && i < 11) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      if (resc) rescale_o(alpha);  // after P V of block b-1, before that of block b
+    }
+    read_v(vl + (kNB - 1) * kBlk * G_::kVStride, pend_v);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) pend_p[kk] = pb[kNB - 1][kk];
+    pending = true;
+  };
+
+  // Any other stage (diagonal, window edge, ragged end): block by block, with the
+  // visibility and mask checks.
+  auto edge_stage = [&](int t, const char* kl, const char* vl) {
+    if (pending) {
+      mfma_pv(pend_v, pend_p);
+      pending = false;
+    }
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int k0 = t * kStage + b * kBlk;
       // keys k0.. are all beyond this wave's last row, past T, or below the window of
       // its first row: nothing to do.  The mask is needed where some key is after
       // the first row or below the last row's window.
       const bool active = (!causal || k0 <= qw + 31) && k0 < T &&
-                          (window <= 0 || k0 + kBN - 1 > qw - window);
-      const bool diag = causal ? (k0 + kBN - 1 > qw || (window > 0 && k0 <= qw + 31 - window))
-                               : (k0 + kBN > T);
-      f32x16 s[2];
-      bf16x8 vf[2][2][G_::kDBlocks];
-      if (active) part_a(k0, cur + sub * kBN * G_::kKStride, cur + G_::kKTile + sub * kBN * G_::kVStride, s, vf);
-      if (sub == kSub - 1) {
-        asm volatile("" ::: "memory");
-        if (t + 1 < nstages) stage(t + 1, nxt);  // that array was freed by the last barrier
-      }
-      if (active) part_b(k0, diag, s, vf);
+                          (window <= 0 || k0 + kBlk - 1 > qw - window);
+      if (!active) continue;
+      const bool diag = causal ? (k0 + kBlk - 1 > qw || (window > 0 && k0 <= qw + 31 - window))
+                               : (k0 + kBlk > T);
+      bf16x8 kf[KS];
+      read_k(kl + b * kBlk * G_::kKStride, kf);
+      f32x16 s;
+      mfma_s(kf, s);
+      if (diag) mask_blk(s, k0);
+      bf16x8 pb[2];
+      float alpha;
+      if (softmax_blk(s, pb, alpha)) rescale_o(alpha);
+      bf16x8 vf[2][DB];
+      read_v(vl + b * kBlk * G_::kVStride, vf);
+      mfma_pv(vf, pb);
     }
+  };
+
+  // Stages alternate between the two LDS arrays.  Stage t+1's loads are in flight
+  // while stage t is computed; right after the barrier that ends stage t (every wave
+  // has read it) stage t+2's loads go into the array stage t held.
+  auto step = [&](int t, char* cur) {
+    const int ks = t * kStage;
+    bool inter = ks + kStage <= T;
+    if (causal) inter = inter && ks + kStage - 1 <= qw;               // below the diagonal
+    if (WIN && window > 0) inter = inter && ks > qw + 31 - window;    // inside every window
+    if (inter)
+      interior_stage(cur, cur + G_::kKTile);
+    else
+      edge_stage(t, cur, cur + G_::kKTile);
     __builtin_amdgcn_s_waitcnt(0);  // stage t+1 has landed in LDS
     __syncthreads();
+    if (t + 2 < nstages) stage(t + 2, cur);
   };
 
   stage(t0, lds_a);
+  if (t0 + 1 < nstages) stage(t0 + 1, lds_b);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = t0; t < nstages; t += 2) {
-    step(t, lds_a, lds_b);
-    if (t + 1 < nstages) step(t + 1, lds_b, lds_a);
+    step(t, lds_a);
+    if (t + 1 < nstages) step(t + 1, lds_b);
   }
-
+  if (pending) mfma_pv(pend_v, pend_p);
   // epilogue: O^T row (head dim) of accumulator r in block db is
   // 32*db + 8*(r/4) + 4*half + r%4; column is this lane's query.
   const float inv = 1.f / pair_sum(l_part);
