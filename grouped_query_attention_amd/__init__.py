@@ -26,7 +26,8 @@ GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
 EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_prefill_window", "attn_decode_workspace_bytes",
             "attn_decode_num_splits", "attn_decode_cached", "attn_decode_window_workspace_bytes",
             "attn_decode_window", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
-            "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_strerror")
+            "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_kv_append",
+            "attn_kv_append_paged", "attn_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgqa_attn.so is not built (%s); run python grouped_query_attention_amd/build.py"
@@ -60,6 +61,11 @@ lib.attn_decode_paged_window_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i,
 lib.attn_decode_paged_window.restype = _i
 lib.attn_decode_paged_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                          _i, _i, _vp, _sz, _vp]
+lib.attn_kv_append.restype = _i
+lib.attn_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]
+lib.attn_kv_append_paged.restype = _i
+lib.attn_kv_append_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                                     _i, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
@@ -244,3 +250,60 @@ def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspac
     if rc != GQA_OK:
         raise GQAError(rc, what)
     return out
+
+
+def _append_inputs(k_new, v_new, cache, freq_factors, rope_base):
+    if k_new.dtype != torch.float32 or v_new.dtype != torch.float32:
+        raise TypeError("k_new and v_new must be float32")
+    if k_new.dim() != 4 or v_new.shape != k_new.shape:
+        raise ValueError("k_new, v_new must be [B, newTokens, Hkv, d]; got %s %s"
+                         % (tuple(k_new.shape), tuple(v_new.shape)))
+    d = k_new.shape[3]
+    ff = None
+    if freq_factors is not None and rope_base:
+        if freq_factors.dtype != torch.float32 or tuple(freq_factors.shape) != (d // 2,):
+            raise ValueError("freq_factors must be float32 [d/2]")
+        ff = _dev_ptr(freq_factors, "freq_factors")
+    return ff, _dtype_code(cache)
+
+
+def attn_kv_append(k_new, v_new, kcache, vcache, start_pos, rope_base=0.0, freq_factors=None,
+                   stream=None):
+    """Write the new tokens k_new, v_new [B,n,Hkv,d] float32 into kcache, vcache
+    [B,Hkv,L,d] (float32 or bfloat16) at rows start_pos .. start_pos+n-1, rotating K with
+    NeoX RoPE at each token's position when rope_base > 0 (attn_kv_append)."""
+    B, n, Hkv, d = k_new.shape
+    if kcache.dim() != 4 or vcache.shape != kcache.shape or kcache.dtype != vcache.dtype:
+        raise ValueError("kcache, vcache must be [B, Hkv, L, d] of one dtype")
+    if kcache.shape[0] != B or kcache.shape[1] != Hkv or kcache.shape[3] != d:
+        raise ValueError("cache %s does not match new tokens %s" % (tuple(kcache.shape), tuple(k_new.shape)))
+    ff, dt = _append_inputs(k_new, v_new, kcache, freq_factors, rope_base)
+    rc = lib.attn_kv_append(_dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), _dev_ptr(kcache, "kcache"),
+                            _dev_ptr(vcache, "vcache"), ff, B, n, Hkv, d, kcache.shape[2], int(start_pos),
+                            float(rope_base), dt, _stream_handle(stream, k_new.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_kv_append")
+
+
+def attn_kv_append_paged(k_new, v_new, kpool, vpool, block_table, seq_lens, rope_base=0.0,
+                         freq_factors=None, stream=None):
+    """Paged append: the new tokens of sequence b are its last n positions of seq_lens[b],
+    stored through block_table [B,max_blocks] int32 into kpool, vpool
+    [num_blocks,Hkv,block_size,d] (attn_kv_append_paged)."""
+    B, n, Hkv, d = k_new.shape
+    if kpool.dim() != 4 or vpool.shape != kpool.shape or kpool.dtype != vpool.dtype:
+        raise ValueError("kpool, vpool must be [num_blocks, Hkv, block_size, d] of one dtype")
+    if kpool.shape[1] != Hkv or kpool.shape[3] != d:
+        raise ValueError("pool %s does not match new tokens %s" % (tuple(kpool.shape), tuple(k_new.shape)))
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    ff, dt = _append_inputs(k_new, v_new, kpool, freq_factors, rope_base)
+    rc = lib.attn_kv_append_paged(_dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), _dev_ptr(kpool, "kpool"),
+                                  _dev_ptr(vpool, "vpool"), _dev_ptr(block_table, "block_table"),
+                                  _dev_ptr(seq_lens, "seq_lens"), ff, B, n, Hkv, d, kpool.shape[2],
+                                  block_table.shape[1], kpool.shape[0], float(rope_base), dt,
+                                  _stream_handle(stream, k_new.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_kv_append_paged")

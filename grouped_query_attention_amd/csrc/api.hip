@@ -157,6 +157,20 @@ int paged_impl(const void* q, const void* kpool, const void* vpool,
   return status_of(gqa::launch_attn_decode_paged(a, pg, plan, static_cast<hipStream_t>(stream)));
 }
 
+// Host checks shared by both append entry points.
+int append_check(const float* k_new, const float* v_new, const void* kc, const void* vc,
+                 const float* freq_factors, int B, int newTokens, int Hkv, int d_h, float rope_base,
+                 int dtype) {
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_EINVAL;
+  if (B < 0 || newTokens < 0 || Hkv <= 0 || d_h <= 0) return GQA_EINVAL;
+  if (!(rope_base >= 0.f) || !isfinite(rope_base)) return GQA_EINVAL;
+  if (d_h > kMaxHeadDim || d_h % 8 != 0) return GQA_EUNSUPPORTED;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kc) || !aligned16(vc)) return GQA_EINVAL;
+  if (freq_factors && rope_base > 0.f && !aligned4(freq_factors)) return GQA_EINVAL;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +263,39 @@ int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool
   return paged_impl(q, kpool, vpool, block_table, seq_lens, out, B, newTokens, Hq, Hkv, d_h,
                     block_size, max_blocks, num_blocks, window, dtype, workspace, workspace_bytes,
                     stream);
+}
+
+int attn_kv_append(const float* k_new, const float* v_new, void* kcache, void* vcache,
+                   const float* freq_factors, int B, int newTokens, int Hkv, int d_h, int totalLen,
+                   int start_pos, float rope_base, int dtype, void* stream) {
+  int rc = append_check(k_new, v_new, kcache, vcache, freq_factors, B, newTokens, Hkv, d_h, rope_base,
+                        dtype);
+  if (rc != GQA_OK) return rc;
+  if (totalLen < 0 || start_pos < 0 || (long long)start_pos + newTokens > totalLen) return GQA_EINVAL;
+  if (totalLen > kMaxSeq) return GQA_EUNSUPPORTED;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  gqa::KvAppendArgs a{k_new, v_new, kcache, vcache, freq_factors, dtype, B, newTokens, Hkv, d_h,
+                      totalLen, start_pos, nullptr, nullptr, 0, 0, 0, rope_base > 0.f ? 1 : 0,
+                      rope_base > 0.f ? log2((double)rope_base) : 0.0};
+  return status_of(gqa::launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_kv_append_paged(const float* k_new, const float* v_new, void* kpool, void* vpool,
+                         const int* block_table, const int* seq_lens, const float* freq_factors, int B,
+                         int newTokens, int Hkv, int d_h, int block_size, int max_blocks,
+                         int num_blocks, float rope_base, int dtype, void* stream) {
+  int rc = append_check(k_new, v_new, kpool, vpool, freq_factors, B, newTokens, Hkv, d_h, rope_base,
+                        dtype);
+  if (rc != GQA_OK) return rc;
+  if (block_size < 0 || max_blocks < 0 || num_blocks < 0) return GQA_EINVAL;
+  if ((long long)max_blocks * block_size > kMaxSeq) return GQA_EINVAL;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (block_size == 0 || max_blocks == 0 || num_blocks == 0) return GQA_EINVAL;
+  if (!aligned4(block_table) || !aligned4(seq_lens)) return GQA_EINVAL;
+  gqa::KvAppendArgs a{k_new, v_new, kpool, vpool, freq_factors, dtype, B, newTokens, Hkv, d_h, 0, 0,
+                      block_table, seq_lens, block_size, max_blocks, num_blocks, rope_base > 0.f ? 1 : 0,
+                      rope_base > 0.f ? log2((double)rope_base) : 0.0};
+  return status_of(gqa::launch_kv_append(a, static_cast<hipStream_t>(stream)));
 }
 
 const char* attn_strerror(int code) {

@@ -79,4 +79,25 @@ struct PagedArgs {
 hipError_t launch_attn_decode_paged(const DecodeArgs& a, const PagedArgs& pg, const DecodePlan& p,
                                     hipStream_t stream);
 
+// KV-cache append with NeoX RoPE on K.  k_new/v_new [B, n, Hkv, d] fp32; kc/vc the cache
+// [B, Hkv, L, d] (table == nullptr, rows start_pos..) or the paged pools
+// [num_blocks, Hkv, block_size, d] (rows seq_lens[b]-n.. through the block table).
+// d is a multiple of 8.  rope = 0 writes K unrotated.
+struct KvAppendArgs {
+  const float* k_new;
+  const float* v_new;
+  void* kc;
+  void* vc;
+  const float* freq_factors;  // [d/2] or nullptr
+  int dtype;                  // of the cache
+  int B, n, Hkv, d;
+  int L, start_pos;                                // contiguous cache
+  const int* table;                                // paged: [B, max_blocks], or nullptr
+  const int* seq_lens;                             // paged: [B]
+  int block_size, max_blocks, num_blocks;          // paged
+  int rope;
+  double log2_base;                                // log2 of the RoPE base
+};
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+
 }  // namespace gqa

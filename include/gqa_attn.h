@@ -204,6 +204,53 @@ int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool
                              int max_blocks, int num_blocks, int window, int dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KV-cache append with NeoX rotary embedding on K: the step right before cached decode
+ * (Hesper's attention layer, the fused RoPE-K + KV-cache-write kernels and their batched
+ * prefill companion; the forge chapter's apply_rope at offset start_pos, then the cache
+ * append).  New token i of sequence b, at absolute position p = start_pos + i, is written
+ * to cache row p of every K/V head:
+ *
+ *   vcache[b,g,p,:] = v_new[b,i,g,:]
+ *   kcache[b,g,p,j]       = k1 * cos(a_j) - k2 * sin(a_j)      for j < d_h/2, with
+ *   kcache[b,g,p,j+d_h/2] = k2 * cos(a_j) + k1 * sin(a_j)      k1 = k_new[b,i,g,j],
+ *                                                              k2 = k_new[b,i,g,j+d_h/2],
+ *   a_j = p * rope_base^(-2j/d_h) / freq_factors[j]
+ *
+ * (the pages pair dim j with dim j + d_h/2 and name a base and per-pair frequency
+ * factors; the angle above is the plain reading of that rotation).
+ *   k_new, v_new   [B, newTokens, Hkv, d_h] float32, token-major (the projections' layout)
+ *   kcache, vcache [B, Hkv, totalLen, d_h] of dtype; bf16 values are rounded to nearest
+ *                  even from the float32 result.  Rows other than start_pos ..
+ *                  start_pos+newTokens-1 are not touched.
+ *   freq_factors   [d_h/2] float32 (4-byte aligned) or NULL for all ones; read only when
+ *                  rope_base > 0
+ *   rope_base      > 0 rotates K; 0 writes K unrotated
+ * Angles are formed in double precision and reduced modulo 2*pi; the rotation is float32.
+ * Errors: GQA_EINVAL for negative sizes, Hkv <= 0, start_pos + newTokens > totalLen, a
+ * negative or non-finite rope_base, null or misaligned pointers; GQA_EUNSUPPORTED for d_h
+ * not a multiple of 8 or above 256.
+ */
+int attn_kv_append(const float* k_new, const float* v_new, void* kcache, void* vcache,
+                   const float* freq_factors, int B, int newTokens, int Hkv, int d_h, int totalLen,
+                   int start_pos, float rope_base, int dtype, void* stream);
+
+/*
+ * The same append into paged pools [num_blocks, Hkv, block_size, d_h] (the layout of
+ * attn_decode_paged): the new tokens of sequence b are its last newTokens positions,
+ * p = seq_lens[b] - newTokens + i, stored in block block_table[b][p / block_size] at row
+ * p % block_size.  block_table [B, max_blocks] and seq_lens [B] are int32 device arrays.
+ * A sequence whose length is below newTokens or beyond max_blocks*block_size, or whose
+ * needed table entry lies outside [0, num_blocks), is not written (the device-side
+ * metadata cannot be checked before launch).  The blocks receiving new tokens must not be
+ * shared between sequences (concurrent writes to one row race).  Other errors as
+ * attn_kv_append, plus GQA_EINVAL for non-positive block_size, max_blocks or num_blocks.
+ */
+int attn_kv_append_paged(const float* k_new, const float* v_new, void* kpool, void* vpool,
+                         const int* block_table, const int* seq_lens, const float* freq_factors,
+                         int B, int newTokens, int Hkv, int d_h, int block_size, int max_blocks,
+                         int num_blocks, float rope_base, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* attn_strerror(int code);
 

@@ -212,3 +212,43 @@ def test_window_workspace_follows_the_window():
         assert p == w
     # a window wider than the history plans the history
     assert gqa.attn_decode_window_workspace_bytes(B, n, L, Hq, Hkv, d, 10 * L) == full
+
+
+def kv_append(kn=A16, vn=A16, kc=A16, vc=A16, ff=None, B=1, n=2, Hkv=2, d=16, L=8, sp=6, base=10000.0,
+              dtype=BF16):
+    return lib.attn_kv_append(kn, vn, kc, vc, ff, B, n, Hkv, d, L, sp, ctypes.c_float(base), dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sp=7), EINVAL),                   # start_pos + newTokens > totalLen
+    (dict(sp=-1), EINVAL),
+    (dict(n=-1), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(Hkv=0), EINVAL),
+    (dict(d=12), EUNSUP),                   # not a multiple of 8
+    (dict(d=264), EUNSUP),
+    (dict(base=-1.0), EINVAL),
+    (dict(base=float("inf")), EINVAL),
+    (dict(base=float("nan")), EINVAL),
+    (dict(dtype=5), EINVAL),
+    (dict(kc=None), EINVAL),
+    (dict(vn=A16 + 4), EINVAL),             # misaligned
+    (dict(ff=A16 + 2), EINVAL),             # freq factors not 4-byte aligned
+    (dict(B=0), OK),                        # nothing to do
+    (dict(n=0), OK),
+])
+def test_kv_append_rejects(kw, code):
+    assert kv_append(**kw) == code
+
+
+def test_kv_append_paged_rejects():
+    def call(bs=16, mb=4, nb=8, table=A16, lens=A16, n=1, d=16):
+        return lib.attn_kv_append_paged(A16, A16, A16, A16, table, lens, None, 2, n, 2, d, bs, mb, nb,
+                                        ctypes.c_float(10000.0), BF16, None)
+    assert call(bs=0) == EINVAL
+    assert call(mb=0) == EINVAL
+    assert call(nb=-1) == EINVAL
+    assert call(table=None) == EINVAL
+    assert call(lens=A16 + 2) == EINVAL
+    assert call(d=20) == EUNSUP
+    assert call(n=0) == OK
