@@ -27,7 +27,8 @@ EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_prefill_window", "attn_deco
             "attn_decode_num_splits", "attn_decode_cached", "attn_decode_window_workspace_bytes",
             "attn_decode_window", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
             "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_kv_append",
-            "attn_kv_append_paged", "attn_strerror")
+            "attn_kv_append_paged", "attn_prefill_lse", "attn_backward_workspace_bytes", "attn_backward",
+            "attn_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgqa_attn.so is not built (%s); run python grouped_query_attention_amd/build.py"
@@ -66,6 +67,13 @@ lib.attn_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, 
 lib.attn_kv_append_paged.restype = _i
 lib.attn_kv_append_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                      _i, _vp]
+lib.attn_prefill_lse.restype = _i
+lib.attn_prefill_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+lib.attn_backward_workspace_bytes.restype = _sz
+lib.attn_backward_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+lib.attn_backward.restype = _i
+lib.attn_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
+                              _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
@@ -307,3 +315,64 @@ def attn_kv_append_paged(k_new, v_new, kpool, vpool, block_table, seq_lens, rope
                                   _stream_handle(stream, k_new.device))
     if rc != GQA_OK:
         raise GQAError(rc, "attn_kv_append_paged")
+
+
+def attn_prefill_lse(q, k, v, scale=None, causal=True, out=None, lse=None, stream=None):
+    """Prefill that also returns the row log-sum-exp lse [B,Hq,T] float32 (natural log)."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Hkv, T, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, T) \
+            or lse.dtype != torch.float32:
+        raise ValueError("out must be float32 like q and lse float32 [B, Hq, T]")
+    rc = lib.attn_prefill_lse(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                              _dev_ptr(lse, "lse"), B, Hq, Hkv, T, d, float(scale), int(bool(causal)),
+                              _dtype_code(q), _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_prefill_lse")
+    return out, lse
+
+
+def attn_backward_workspace_bytes(B, Hq, Hkv, T, d, dtype=GQA_BF16) -> int:
+    return int(lib.attn_backward_workspace_bytes(B, Hq, Hkv, T, d, int(dtype)))
+
+
+def attn_backward(q, k, v, out, dout, lse, scale=None, causal=True, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
+    """Gradients (dq, dk, dv) float32 of <dout, attention(q, k, v)> from the forward's
+    out and lse (attn_prefill_lse); q, k, v bf16."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Hkv, T, d] matching q")
+    for t, n in ((out, "out"), (dout, "dout")):
+        if t.shape != q.shape or t.dtype != torch.float32:
+            raise ValueError("%s must be float32 of shape %s" % (n, tuple(q.shape)))
+    if tuple(lse.shape) != (B, Hq, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, T]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty((B, Hkv, T, d), dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty((B, Hkv, T, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    need = attn_backward_workspace_bytes(B, Hq, Hkv, T, d, _dtype_code(q))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.attn_backward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                           _dev_ptr(dout, "dout"), _dev_ptr(lse, "lse"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
+                           _dev_ptr(dv, "dv"), B, Hq, Hkv, T, d, float(scale), int(bool(causal)), _dtype_code(q),
+                           ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_backward")
+    return dq, dk, dv

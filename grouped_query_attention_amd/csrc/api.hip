@@ -29,7 +29,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_EHIP; }
 
 int prefill_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                  int T, int d_h, float scale, int causal, int window, int dtype, int algo,
-                 void* stream) {
+                 void* stream, float* lse = nullptr) {
   int rc = check_common(dtype, B, Hq, Hkv, d_h);
   if (rc != GQA_OK) return rc;
   if (T < 0 || !isfinite(scale) || (causal != 0 && causal != 1)) return GQA_EINVAL;
@@ -45,12 +45,12 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (algo == GQA_ALGO_MFMA || (algo == GQA_ALGO_AUTO && mfma_ok)) {
-    gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window};
+    gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window, lse};
     return status_of(gqa::launch_attn_prefill_mfma(a, s));
   }
   const long long sd = d_h;
   gqa::GenericArgs a{q, k, v, out, dtype, B, Hq, Hkv, T, T, d_h, scale, causal, 0,
-                     (long long)Hq * T * sd, (long long)T * sd, sd, window};
+                     (long long)Hq * T * sd, (long long)T * sd, sd, window, lse};
   return status_of(gqa::launch_attn_generic(a, s));
 }
 
@@ -187,6 +187,12 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, float* out, int
   return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, 0, dtype, algo, stream);
 }
 
+int attn_prefill_lse(const void* q, const void* k, const void* v, float* out, float* lse, int B, int Hq,
+                     int Hkv, int T, int d_h, float scale, int causal, int dtype, void* stream) {
+  if (B > 0 && T > 0 && !aligned4(lse)) return GQA_EINVAL;
+  return prefill_impl(q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, 0, dtype, GQA_ALGO_AUTO, stream, lse);
+}
+
 int attn_prefill_window(const void* q, const void* k, const void* v, float* out, int B, int Hq,
                         int Hkv, int T, int d_h, float scale, int window, int dtype, void* stream) {
   if (window < 1) return GQA_EINVAL;
@@ -263,6 +269,32 @@ int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool
   return paged_impl(q, kpool, vpool, block_table, seq_lens, out, B, newTokens, Hq, Hkv, d_h,
                     block_size, max_blocks, num_blocks, window, dtype, workspace, workspace_bytes,
                     stream);
+}
+
+size_t attn_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d_h, int dtype) {
+  if (check_common(dtype, B, Hq, Hkv, d_h) != GQA_OK || T < 0) return 0;
+  if (!gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv)) return 0;
+  return gqa::backward_workspace_bytes(B, Hq, T, d_h);
+}
+
+int attn_backward(const void* q, const void* k, const void* v, const float* out, const float* dout,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int T, int d_h,
+                  float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(dtype, B, Hq, Hkv, d_h);
+  if (rc != GQA_OK) return rc;
+  if (T < 0 || !isfinite(scale) || (causal != 0 && causal != 1)) return GQA_EINVAL;
+  if (T > kMaxSeq) return GQA_EUNSUPPORTED;
+  if (!gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv)) return GQA_EUNSUPPORTED;
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return GQA_EINVAL;
+  const size_t need = gqa::backward_workspace_bytes(B, Hq, T, d_h);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return GQA_EWORKSPACE;
+  gqa::BackwardArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, T, d_h, scale, causal,
+                      nullptr, nullptr, nullptr};
+  return status_of(gqa::launch_attn_backward_mfma(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int attn_kv_append(const float* k_new, const float* v_new, void* kcache, void* vcache,

@@ -33,7 +33,7 @@ template <typename T, int DPL>
 __global__ __launch_bounds__(256) void attn_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ out, int Hq, int Hkv, int Tq, int Tk, int d, float scale_log2, int causal,
-    int pos0, int window, long long q_sb, long long q_sh, long long q_st) {
+    int pos0, int window, long long q_sb, long long q_sh, long long q_st, float* __restrict__ lse) {
   constexpr int DP = DPL * kLanesPerRow;  // padded head dim held by one row
   __shared__ float Ks[kKeysPerTile * DP];
   __shared__ float Vs[kKeysPerTile * DP];
@@ -116,6 +116,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
 
   if (row_ok) {
     const float inv = 1.f / l;
+    // row log-sum-exp of the scaled scores, natural log: (m + log2 l) * ln 2
+    if (lse && c == 0) lse[((long long)b * Hq + h) * Tq + i] = (m + __log2f(l)) * 0.6931471805599453f;
 #pragma unroll
     for (int u = 0; u < DPL; ++u) {
       const int e = c + kLanesPerRow * u;
@@ -131,7 +133,7 @@ hipError_t launch_t(const GenericArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.out, a.Hq, a.Hkv, a.Tq, a.Tk, a.d,
                      a.scale * 1.4426950408889634f, a.causal, a.pos0, a.window, a.q_sb, a.q_sh,
-                     a.q_st);
+                     a.q_st, a.lse);
   return hipGetLastError();
 }
 

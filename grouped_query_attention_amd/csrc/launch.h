@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace gqa {
 
@@ -25,6 +26,7 @@ struct GenericArgs {
   int pos0;
   long long q_sb, q_sh, q_st;  // strides of q and out: batch, head, row
   int window;                  // local window (causal only); 0 = none
+  float* lse;                  // [B, Hq, Tq] row log-sum-exp (natural log), or nullptr
 };
 hipError_t launch_attn_generic(const GenericArgs& a, hipStream_t stream);
 
@@ -38,6 +40,7 @@ struct PrefillArgs {
   float scale;
   int causal;
   int window;  // local window (causal only); 0 = none
+  float* lse;  // [B, Hq, T] row log-sum-exp (natural log), or nullptr
 };
 bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
@@ -99,5 +102,28 @@ struct KvAppendArgs {
   double log2_base;                                // log2 of the RoPE base
 };
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+
+// Backward pass of causal GQA prefill on bf16 matrix cores.  q/out/dout/dq [B,Hq,T,d],
+// k/v/dk/dv [B,Hkv,T,d], lse [B,Hq,T] (natural log, from the forward pass); d a
+// multiple of 16, <= 128.  dob, lse2, Dv point into the workspace.
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* out;
+  const float* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, Hq, Hkv, T, d;
+  float scale;
+  int causal;
+  uint16_t* dob;  // [B,Hq,T,d] dO rounded to bf16
+  float* lse2;    // [B,Hq,T] lse in log2 units
+  float* Dv;      // [B,Hq,T] rowsum(dO * O)
+};
+size_t backward_workspace_bytes(int B, int Hq, int T, int d);
+hipError_t launch_attn_backward_mfma(BackwardArgs a, void* workspace, hipStream_t stream);
 
 }  // namespace gqa

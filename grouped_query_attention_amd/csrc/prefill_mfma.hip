@@ -90,7 +90,8 @@ template <int D, int HPW, bool WIN>
 __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int Hq, int Hkv, int T, float c,
-    unsigned qsign, int causal, int window_arg, int n_qtiles, int n_hgroups, int B) {
+    unsigned qsign, int causal, int window_arg, int n_qtiles, int n_hgroups, int B,
+    float* __restrict__ lse) {
   using G_ = Geo<D>;
   // the local window is a separate instantiation: plain causal attention carries none
   // of its checks
@@ -414,7 +415,12 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   if (pending) mfma_pv(pend_v, pend_p);
   // epilogue: O^T row (head dim) of accumulator r in block db is
   // 32*db + 8*(r/4) + 4*half + r%4; column is this lane's query.
-  const float inv = 1.f / pair_sum(l_part);
+  const float l_row = pair_sum(l_part);
+  const float inv = 1.f / l_row;
+  // row log-sum-exp of the scaled scores, natural log: (m + log2 l) * ln 2 (m is the
+  // reference the p were taken against, in log2 units)
+  if (lse && qi < T && half == 0)
+    lse[((long long)b * Hq + h) * T + qi] = (m_run + __log2f(l_row)) * 0.6931471805599453f;
   if (qi < T) {
     float* orow = out + (((long long)b * Hq + h) * T + qi) * D;
 #pragma unroll
@@ -446,7 +452,7 @@ hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW, WIN>), dim3((unsigned)nblocks), dim3(kWgWaves * 64), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, a.Hq, a.Hkv, a.T, c, qsign, a.causal,
-                     a.causal ? a.window : 0, n_qtiles, n_hgroups, a.B);
+                     a.causal ? a.window : 0, n_qtiles, n_hgroups, a.B, a.lse);
   return hipGetLastError();
 }
 

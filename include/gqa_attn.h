@@ -205,6 +205,41 @@ int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill that also returns each row's softmax statistic, the input of attn_backward
+ * (Riftco "Two exact full-sequence algorithms": the memory-linear path keeps per-row
+ * statistics of shape [B, H, T] instead of the probabilities).  As attn_prefill (automatic
+ * kernel choice, window 0), plus
+ *   lse  [B, Hq, T] float32, 4-byte aligned: log sum_j exp(s_ij) over the row's visible
+ *        keys, natural log, with s_ij = scale * <q_i, k_j> as in out; P_ij = exp(s_ij - lse_i).
+ * The page keeps the row maximum and the exponential sum; their log-sum-exp carries the
+ * same information in one number.  Errors as attn_prefill, plus GQA_EINVAL for a null or
+ * misaligned lse.
+ */
+int attn_prefill_lse(const void* q, const void* k, const void* v, float* out, float* lse, int B, int Hq,
+                     int Hkv, int T, int d_h, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Backward pass of prefill (Riftco "Two exact full-sequence algorithms": recompute each
+ * probability from Q, K and the row statistic, then apply the exact softmax
+ * vector-Jacobian product).  Given the forward's inputs, its output `out`, its `lse`
+ * (attn_prefill_lse) and the upstream gradient dout = dL/dout, writes the gradients of L:
+ *   dq [B,Hq,T,d_h] = scale * sum_j dS_ij k_j
+ *   dk [B,Hkv,T,d_h] = scale * sum over the group's query heads and rows of dS_ij q_i
+ *   dv [B,Hkv,T,d_h] = sum over the group's query heads and rows of P_ij dout_i
+ * with P_ij = exp(s_ij - lse_i), dS_ij = P_ij (dout_i . v_j - dout_i . out_i).
+ *   q, k, v  bf16, as the forward;  out, dout, lse, dq, dk, dv float32
+ *   workspace: device memory of attn_backward_workspace_bytes(...) bytes, 256-byte aligned
+ *   (dout rounded to bf16 for the matrix cores, and two float32 statistics per row)
+ * Built for dtype GQA_BF16 with d_h a multiple of 16, at most 128 (GQA_EUNSUPPORTED
+ * otherwise; the workspace query then returns 0).  Errors as attn_prefill, plus
+ * GQA_EWORKSPACE.  The result is deterministic (no atomics).
+ */
+size_t attn_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d_h, int dtype);
+int attn_backward(const void* q, const void* k, const void* v, const float* out, const float* dout,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int T, int d_h,
+                  float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * KV-cache append with NeoX rotary embedding on K: the step right before cached decode
  * (Hesper's attention layer, the fused RoPE-K + KV-cache-write kernels and their batched
  * prefill companion; the forge chapter's apply_rope at offset start_pos, then the cache

@@ -1,0 +1,164 @@
+"""Row statistics (attn_prefill_lse) and the backward pass (attn_backward) on the GPU
+against the float64 oracle (oracle/backward.py).
+
+* lse from both forward kernels (bf16 matrix cores and the fp32 vector kernel) against
+  the oracle's row log-sum-exp; the output is bitwise that of attn_prefill.
+* dq, dk, dv element by element against the oracle on ragged shapes (T not a multiple
+  of the 32/64/128-row tiles), head dims 32..128 including 80, group sizes 1, 2, 4,
+  causal and not, and at the full GQA prefill workload on sampled head groups.
+  The GPU recomputes P from bf16 Q/K, rounds P, dS and dO to bf16 for the matrix cores
+  and accumulates in fp32; the bar is the bf16-input tolerance 1.5e-2 applied to the
+  gradient scaled by its own size: max|gpu - ref| <= 1.5e-2 * max(1, max|ref|).
+* the oracle's invariants hold on the GPU result: key gradients of a K/V head sum to
+  ~0 over the keys, value gradients sum to the upstream gradient.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from oracle import backward as bw
+
+pytestmark = pytest.mark.gpu
+
+SEED = si.SEED_BASE + 50
+
+
+@pytest.fixture(scope="module")
+def gqa():
+    import grouped_query_attention_amd as m
+    return m
+
+
+def inputs(B, Hq, Hkv, T, d, dtype, seed):
+    q, k, v = si.prefill_inputs(B, Hq, Hkv, T, d, dtype, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(B, Hq, T, d, generator=g, dtype=torch.float32)
+    return q, k, v, dout
+
+
+def close(got, want, rel=1.5e-2):
+    got = got.double().cpu().numpy() if torch.is_tensor(got) else got
+    err = np.abs(got - want).max()
+    bound = rel * max(1.0, np.abs(want).max())
+    assert err <= bound, (float(err), float(bound))
+    return err
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("bf16", 80, True),
+                                            ("f32", 64, True), ("f32", 40, False)])
+def test_lse_matches_oracle(gqa, dtype, d, causal):
+    B, Hq, Hkv, T = 2, 4, 2, 197
+    q, k, v = si.prefill_inputs(B, Hq, Hkv, T, d, dtype, SEED + d)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out, lse = gqa.attn_prefill_lse(qd, kd, vd, scale=d ** -0.5, causal=causal)
+    ref_out = gqa.attn_prefill(qd, kd, vd, scale=d ** -0.5, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    want = bw.lse(q.double().numpy(), k.double().numpy(), d ** -0.5, causal)
+    tol = 1.5e-2 if dtype == "bf16" else 1e-4
+    assert np.abs(lse.cpu().double().numpy() - want).max() <= tol
+
+
+def test_lse_worked_example(gqa):
+    """The primer's example through the fp32 kernel: row 2 of q = (1,0) over keys
+    (1,0), (0,1), (1,1), unscaled: lse = log(2e + 1)."""
+    q = torch.zeros(1, 1, 3, 2)
+    q[0, 0, 2] = torch.tensor([1.0, 0.0])
+    k = torch.tensor([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]]).reshape(1, 1, 3, 2)
+    v = torch.tensor([[1.0, 0.0], [2.0, 0.0], [3.0, 0.0]]).reshape(1, 1, 3, 2)
+    out, lse = gqa.attn_prefill_lse(q.cuda(), k.cuda(), v.cuda(), scale=1.0, causal=True)
+    torch.cuda.synchronize()
+    assert abs(lse[0, 0, 2].item() - math.log(2 * math.e + 1)) <= 1e-6
+    assert abs(out[0, 0, 2, 0].item() - 2.0) <= 1e-6
+
+
+CASES = [
+    # B, Hq, Hkv, T, d, causal
+    (2, 4, 2, 200, 128, True),
+    (1, 4, 1, 333, 64, True),
+    (2, 2, 2, 130, 80, True),
+    (1, 8, 2, 257, 32, False),
+    (2, 3, 3, 64, 128, False),
+    (1, 2, 1, 45, 16, True),
+    (1, 16, 8, 512, 128, True),
+    (1, 2, 2, 1, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_T%d_d%d_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full"))
+def test_backward_matches_oracle(gqa, case):
+    B, Hq, Hkv, T, d, causal = case
+    q, k, v, dout = inputs(B, Hq, Hkv, T, d, "bf16", SEED + 7 * T + d)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    scale = d ** -0.5
+    out, lse = gqa.attn_prefill_lse(qd, kd, vd, scale=scale, causal=causal)
+    dq, dk, dv = gqa.attn_backward(qd, kd, vd, out, dout.cuda(), lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    wq, wk, wv = bw.backward(q.double().numpy(), k.double().numpy(), v.double().numpy(), dout.double().numpy(),
+                             scale, causal)
+    close(dq, wq)
+    close(dk, wk)
+    close(dv, wv)
+    # invariants of the exact gradients hold to the same bar
+    G = Hq // Hkv
+    dks = dk.double().cpu().numpy().sum(axis=2)
+    assert np.abs(dks).max() <= 1.5e-2 * max(1.0, np.abs(wk).max()) * math.sqrt(T)
+    dvs = dv.double().cpu().numpy().sum(axis=2)
+    want_dvs = dout.double().numpy().reshape(B, Hkv, G, T, d).sum(axis=(2, 3))
+    assert np.abs(dvs - want_dvs).max() <= 1.5e-2 * max(1.0, np.abs(want_dvs).max())
+
+
+def test_backward_deterministic_and_inputs_untouched(gqa):
+    B, Hq, Hkv, T, d = 1, 4, 2, 300, 128
+    q, k, v, dout = inputs(B, Hq, Hkv, T, d, "bf16", SEED + 3)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), dout.cuda()
+    out, lse = gqa.attn_prefill_lse(qd, kd, vd)
+    r1 = gqa.attn_backward(qd, kd, vd, out, dod, lse)
+    r2 = gqa.attn_backward(qd, kd, vd, out, dod, lse)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(r1, r2))
+    assert torch.equal(qd.cpu(), q) and torch.equal(dod.cpu(), dout)
+
+
+def test_backward_rejects(gqa):
+    q = torch.zeros(1, 2, 8, 40, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 1, 8, 40, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros(1, 2, 8, 40, device="cuda")
+    lse = torch.zeros(1, 2, 8, device="cuda")
+    with pytest.raises(gqa.GQAError):  # d = 40: not a multiple of 16
+        gqa.attn_backward(q, k, k, o, o, lse)
+    assert gqa.attn_backward_workspace_bytes(1, 2, 1, 8, 40) == 0
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros(1, 2, 8, 64, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gqa.GQAError):
+        gqa.attn_backward(q, k, k, o, o, lse, workspace=small)
+
+
+def test_full_size_backward_sampled_groups(gqa):
+    """The GQA prefill workload (B=2, 16 query / 8 K/V heads, T=4096, d=128, bf16) in the
+    launch configuration the benchmark times; two sampled (batch, K/V head) groups checked
+    in full against the oracle restricted to that group."""
+    cfg = si.C3_GQA
+    q, k, v = si.prefill_config_inputs(cfg)
+    g = torch.Generator().manual_seed(cfg.seed + 100)
+    dout = torch.randn(cfg.B, cfg.Hq, cfg.T, cfg.d, generator=g, dtype=torch.float32)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out, lse = gqa.attn_prefill_lse(qd, kd, vd, scale=cfg.scale, causal=True)
+    dq, dk, dv = gqa.attn_backward(qd, kd, vd, out, dout.cuda(), lse, scale=cfg.scale, causal=True)
+    torch.cuda.synchronize()
+    G = cfg.Hq // cfg.Hkv
+    for b, gk in ((0, 0), (1, cfg.Hkv - 1)):
+        hs = slice(gk * G, (gk + 1) * G)
+        wq, wk, wv = bw.backward(q[b:b + 1, hs].double().numpy(), k[b:b + 1, gk:gk + 1].double().numpy(),
+                                 v[b:b + 1, gk:gk + 1].double().numpy(), dout[b:b + 1, hs].double().numpy(),
+                                 cfg.scale, True)
+        close(dq[b:b + 1, hs], wq)
+        close(dk[b:b + 1, gk:gk + 1], wk)
+        close(dv[b:b + 1, gk:gk + 1], wv)
