@@ -157,6 +157,13 @@ int paged_impl(const void* q, const void* kpool, const void* vpool,
   return status_of(gqa::launch_attn_decode_paged(a, pg, plan, static_cast<hipStream_t>(stream)));
 }
 
+// Inverse frequencies of the rotation pairs, base^(-2j/d) in double (the kernel divides
+// by the per-pair factors and multiplies by the position).
+void fill_inv_freq(gqa::KvAppendArgs& a, float rope_base) {
+  if (!a.rope) return;
+  for (int j = 0; j < a.d / 2; ++j) a.inv_freq[j] = pow((double)rope_base, -2.0 * j / a.d);
+}
+
 // Host checks shared by both append entry points.
 int append_check(const float* k_new, const float* v_new, const void* kc, const void* vc,
                  const float* freq_factors, int B, int newTokens, int Hkv, int d_h, float rope_base,
@@ -307,8 +314,8 @@ int attn_kv_append(const float* k_new, const float* v_new, void* kcache, void* v
   if (totalLen > kMaxSeq) return GQA_EUNSUPPORTED;
   if (B == 0 || newTokens == 0) return GQA_OK;
   gqa::KvAppendArgs a{k_new, v_new, kcache, vcache, freq_factors, dtype, B, newTokens, Hkv, d_h,
-                      totalLen, start_pos, nullptr, nullptr, 0, 0, 0, rope_base > 0.f ? 1 : 0,
-                      rope_base > 0.f ? log2((double)rope_base) : 0.0};
+                      totalLen, start_pos, nullptr, nullptr, 0, 0, 0, rope_base > 0.f ? 1 : 0, {}};
+  fill_inv_freq(a, rope_base);
   return status_of(gqa::launch_kv_append(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -325,8 +332,8 @@ int attn_kv_append_paged(const float* k_new, const float* v_new, void* kpool, vo
   if (block_size == 0 || max_blocks == 0 || num_blocks == 0) return GQA_EINVAL;
   if (!aligned4(block_table) || !aligned4(seq_lens)) return GQA_EINVAL;
   gqa::KvAppendArgs a{k_new, v_new, kpool, vpool, freq_factors, dtype, B, newTokens, Hkv, d_h, 0, 0,
-                      block_table, seq_lens, block_size, max_blocks, num_blocks, rope_base > 0.f ? 1 : 0,
-                      rope_base > 0.f ? log2((double)rope_base) : 0.0};
+                      block_table, seq_lens, block_size, max_blocks, num_blocks, rope_base > 0.f ? 1 : 0, {}};
+  fill_inv_freq(a, rope_base);
   return status_of(gqa::launch_kv_append(a, static_cast<hipStream_t>(stream)));
 }
 

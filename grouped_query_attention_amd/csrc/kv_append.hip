@@ -9,14 +9,16 @@
 //
 // Mapping: the work is HBM-bound (read two fp32 rows, write two cache rows), so the
 // layout decides everything.  A thread owns 4 consecutive pairs (8 head dims: j..j+3 and
-// j+d/2..j+d/2+3) of one token and walks the token's K/V heads, so its angles and their
-// sines and cosines are computed once per token, not once per head.  Sixteen-byte loads
-// of the fp32 rows and 8-byte (bf16) or 16-byte (fp32) stores keep every access
-// coalesced: the threads of one token cover a head's row contiguously.
+// j+d/2..j+d/2+3) of one token and kHeadsPerThread of its K/V heads, so its angles and
+// their sines and cosines serve several heads while enough threads stay in flight to
+// cover HBM latency.  Sixteen-byte loads of the fp32 rows and 8-byte (bf16) or 16-byte
+// (fp32) stores keep every access coalesced: the threads of one token cover a head's row
+// contiguously.
 //
 // Angles are formed in double precision (the position times the pair's inverse
-// frequency, reduced modulo 2*pi), so their error does not grow with the position; the
-// reduced angle's sine and cosine and the rotation itself are fp32.
+// frequency, computed on the host in double, reduced modulo 2*pi), so their error does
+// not grow with the position; the reduced angle's sine and cosine and the rotation
+// itself are fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -30,12 +32,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+constexpr int kHeadsPerThread = 2;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 // cos and sin of the angle of pair j at position p
-__device__ __forceinline__ void pair_sincos(long long p, int j, int d, double log2_base,
+__device__ __forceinline__ void pair_sincos(long long p, int j, const double* inv_freq,
                                             const float* __restrict__ ff, float& cs, float& sn) {
-  double inv = exp2(-(2.0 * j / d) * log2_base);
+  double inv = inv_freq[j];
   if (ff) inv /= (double)ff[j];
   const double ang = (double)p * inv;
   const double r = ang - rint(ang / kTwoPi) * kTwoPi;  // |r| <= pi
@@ -52,17 +55,21 @@ __device__ __forceinline__ void store4(void* base, long long off, f32x4 x) {
   }
 }
 
-// One thread: token (b, i), pairs 4*t .. 4*t+3, every K/V head.  PAGED resolves the
+// One thread: token (b, i), pairs 4*t .. 4*t+3, heads kHeadsPerThread*hg ...  PAGED resolves the
 // cache row through the block table; a sequence whose length or table entry does not
 // fit is not written.
 template <bool BF16, bool PAGED>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
   const int half = a.d / 2;
-  const int tpt = half / 4;  // threads per token
+  const int tpt = half / 4;  // threads per (token, head group)
+  const int nhg = (a.Hkv + kHeadsPerThread - 1) / kHeadsPerThread;
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
-  const long long tok = gid / tpt;
-  if (tok >= (long long)a.B * a.n) return;
-  const int t = (int)(gid - tok * tpt);
+  const long long unit = gid / tpt;  // (token, head group)
+  if (unit >= (long long)a.B * a.n * nhg) return;
+  const int t = (int)(gid - unit * tpt);
+  const long long tok = unit / nhg;
+  const int h0 = (int)(unit - tok * nhg) * kHeadsPerThread;
+  const int h1 = min(a.Hkv, h0 + kHeadsPerThread);
   const int b = (int)(tok / a.n), i = (int)(tok - (long long)b * a.n);
   const int j0 = 4 * t;
 
@@ -86,11 +93,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
   float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.rope) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pair_sincos(p, j0 + e, a.d, a.log2_base, a.freq_factors, cs[e], sn[e]);
+    for (int e = 0; e < 4; ++e) pair_sincos(p, j0 + e, a.inv_freq, a.freq_factors, cs[e], sn[e]);
   }
 
   const long long src0 = tok * a.Hkv * a.d;  // [B, n, Hkv, d]: token tok, head 0
-  for (int h = 0; h < a.Hkv; ++h) {
+  for (int h = h0; h < h1; ++h) {
     const long long src = src0 + (long long)h * a.d;
     const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.k_new + src + j0);
     const f32x4 k2 = *reinterpret_cast<const f32x4*>(a.k_new + src + half + j0);
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
 
 template <bool PAGED>
 hipError_t launch(const KvAppendArgs& a, hipStream_t s) {
-  const long long threads = (long long)a.B * a.n * (a.d / 8);
+  const long long threads = (long long)a.B * a.n * ((a.Hkv + kHeadsPerThread - 1) / kHeadsPerThread) * (a.d / 8);
   const long long blocks = (threads + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.dtype == kBF16)

@@ -99,7 +99,7 @@ struct KvAppendArgs {
   const int* seq_lens;                             // paged: [B]
   int block_size, max_blocks, num_blocks;          // paged
   int rope;
-  double log2_base;                                // log2 of the RoPE base
+  double inv_freq[128];                            // base^(-2j/d), j < d/2 (rope only)
 };
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 
