@@ -235,18 +235,76 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     }
   };
 
+  // A stage every row and key of which is visible to this wave (no mask): the two
+  // 32-row blocks in straight-line code, so the second block's S and dP products can
+  // run beside the first block's exp and dS vector work, and the first block's dV and
+  // dK products beside the second block's.
+  auto compute_fast = [&](const char* buf) __attribute__((always_inline)) {
+    const char* qt = buf;
+    const char* ot = buf + kTile;
+    const float* l2s = reinterpret_cast<const float*>(buf + 2 * kTile);
+    const float* dvs = l2s + kQStage;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x16{};
+      dp[blk] = f32x16{};
+      const char* qrow = qt + (32 * blk + col) * TS + half * 16;
+      const char* orow = ot + (32 * blk + col) * TS + half * 16;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(qrow + st * 32), kf[st], s[blk], 0, 0, 0);
+        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(orow + st * 32), vf[st], dp[blk], 0, 0, 0);
+      }
+    }
+    bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -l2s[qr]));
+        pb[blk][r >> 3][r & 7] = (__bf16)p;
+        sb[blk][r >> 3][r & 7] = (__bf16)(p * (dp[blk][r] - dvs[qr]));
+      }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const char* ot16 = ot + (32 * blk + 16 * kk) * TS;
+        const char* qt16 = qt + (32 * blk + 16 * kk) * TS;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(ot16, lane, db), pb[blk][kk], dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(qt16, lane, db), sb[blk][kk], dka[db], 0, 0, 0);
+        }
+      }
+  };
+  // every row of the stage is at or after this wave's last key, inside T, and every key
+  // of the wave is inside T
+  auto stage_interior = [&](int si) __attribute__((always_inline)) {
+    const int r0 = (qs0 + si % per_head) * kQStage;
+    return (!causal || r0 >= kw + 31) && r0 + kQStage <= T && kw + 32 <= T;
+  };
+  auto run = [&](int si, const char* buf) __attribute__((always_inline)) {
+    if (stage_interior(si))
+      compute_fast(buf);
+    else
+      compute(si, buf);
+  };
+
   if (nstages > 0) {
     stage(0, lds_a);
     if (nstages > 1) stage(1, lds_b);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int si = 0; si < nstages; si += 2) {
-      compute(si, lds_a);
+      run(si, lds_a);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (si + 2 < nstages) stage(si + 2, lds_a);
       if (si + 1 < nstages) {
-        compute(si + 1, lds_b);
+        run(si + 1, lds_b);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (si + 3 < nstages) stage(si + 3, lds_b);
@@ -371,18 +429,62 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
     }
   };
 
+  // A stage all of whose keys are visible to every row of this wave: both 32-key blocks
+  // in straight-line code (the second block's products beside the first block's vector
+  // work, as in the dK/dV kernel).
+  auto compute_fast = [&](const char* buf) __attribute__((always_inline)) {
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x16{};
+      dp[blk] = f32x16{};
+      const char* krow = buf + (32 * blk + col) * TS + half * 16;
+      const char* vrow = buf + kKT + (32 * blk + col) * RS + half * 16;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(krow + st * 32), qf[st], s[blk], 0, 0, 0);
+        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(vrow + st * 32), of[st], dp[blk], 0, 0, 0);
+      }
+    }
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -l2));
+        sb[blk][r >> 3][r & 7] = (__bf16)(p * (dp[blk][r] - Dq));
+      }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const char* kt16 = buf + (32 * blk + 16 * kk) * TS;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(kt16, lane, db), sb[blk][kk], dqa[db], 0, 0, 0);
+      }
+  };
+  auto run = [&](int t, const char* buf) __attribute__((always_inline)) {
+    const int j0 = t * kKStage;
+    const bool interior = (!causal || j0 + kKStage - 1 <= qw) && j0 + kKStage <= T && qw + 32 <= T;
+    if (interior)
+      compute_fast(buf);
+    else
+      compute(t, buf);
+  };
+
   if (nstages > 0) {
     stage(0, lds_a);
     if (nstages > 1) stage(1, lds_b);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < nstages; t += 2) {
-      compute(t, lds_a);
+      run(t, lds_a);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (t + 2 < nstages) stage(t + 2, lds_a);
       if (t + 1 < nstages) {
-        compute(t + 1, lds_b);
+        run(t + 1, lds_b);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 3 < nstages) stage(t + 3, lds_b);
