@@ -72,18 +72,18 @@ class DecodeConfig:
 
 
 # The five workloads.  Seeds are SEED_BASE + workload number.
-C1_SINGLE_HEAD = PrefillConfig("single_head_b1_h1_t16_d8_f32", 1, 1, 1, 16, 8, "f32", SEED_BASE + 1)
-C2_MHA_F32 = PrefillConfig("mha_b4_h12_t512_d64_f32", 4, 12, 12, 512, 64, "f32", SEED_BASE + 2)
-C2_MHA_BF16 = PrefillConfig("mha_b4_h12_t512_d64_bf16", 4, 12, 12, 512, 64, "bf16", SEED_BASE + 2)
-C3_GQA = PrefillConfig("gqa_b2_hq16_hkv8_t4096_d128_bf16", 2, 16, 8, 4096, 128, "bf16", SEED_BASE + 3)
-C4_BITNET = PrefillConfig("bitnet3b_b8_h32_t2048_d80_bf16", 8, 32, 32, 2048, 80, "bf16", SEED_BASE + 4)
-C5_DECODE_N1 = DecodeConfig("decode_b64_hq32_hkv8_len32768_d128_n1_bf16", 64, 1, 32, 8, 32768, 128,
+SINGLE_HEAD_T16_F32 = PrefillConfig("single_head_b1_h1_t16_d8_f32", 1, 1, 1, 16, 8, "f32", SEED_BASE + 1)
+MHA_T512_F32 = PrefillConfig("mha_b4_h12_t512_d64_f32", 4, 12, 12, 512, 64, "f32", SEED_BASE + 2)
+MHA_T512_BF16 = PrefillConfig("mha_b4_h12_t512_d64_bf16", 4, 12, 12, 512, 64, "bf16", SEED_BASE + 2)
+GQA_T4096 = PrefillConfig("gqa_b2_hq16_hkv8_t4096_d128_bf16", 2, 16, 8, 4096, 128, "bf16", SEED_BASE + 3)
+BITNET3B_T2048 = PrefillConfig("bitnet3b_b8_h32_t2048_d80_bf16", 8, 32, 32, 2048, 80, "bf16", SEED_BASE + 4)
+DECODE_L32768_N1 = DecodeConfig("decode_b64_hq32_hkv8_len32768_d128_n1_bf16", 64, 1, 32, 8, 32768, 128,
                             "bf16", SEED_BASE + 5)
-C5_DECODE_N4 = DecodeConfig("decode_b64_hq32_hkv8_len32768_d128_n4_bf16", 64, 4, 32, 8, 32768, 128,
+DECODE_L32768_N4 = DecodeConfig("decode_b64_hq32_hkv8_len32768_d128_n4_bf16", 64, 4, 32, 8, 32768, 128,
                             "bf16", SEED_BASE + 5)
 
-PREFILL_CONFIGS = [C1_SINGLE_HEAD, C2_MHA_F32, C2_MHA_BF16, C3_GQA, C4_BITNET]
-DECODE_CONFIGS = [C5_DECODE_N1, C5_DECODE_N4]
+PREFILL_CONFIGS = [SINGLE_HEAD_T16_F32, MHA_T512_F32, MHA_T512_BF16, GQA_T4096, BITNET3B_T2048]
+DECODE_CONFIGS = [DECODE_L32768_N1, DECODE_L32768_N4]
 
 
 def torch_dtype(dtype: str):

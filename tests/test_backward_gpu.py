@@ -145,7 +145,7 @@ def test_full_size_backward_sampled_groups(gqa):
     """The GQA prefill workload (B=2, 16 query / 8 K/V heads, T=4096, d=128, bf16) in the
     launch configuration the benchmark times; two sampled (batch, K/V head) groups checked
     in full against the oracle restricted to that group."""
-    cfg = si.C3_GQA
+    cfg = si.GQA_T4096
     q, k, v = si.prefill_config_inputs(cfg)
     g = torch.Generator().manual_seed(cfg.seed + 100)
     dout = torch.randn(cfg.B, cfg.Hq, cfg.T, cfg.d, generator=g, dtype=torch.float32)

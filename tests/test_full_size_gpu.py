@@ -25,7 +25,7 @@ def gqa():
     return m
 
 
-@pytest.mark.parametrize("cfg", [si.C3_GQA, si.C4_BITNET], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [si.GQA_T4096, si.BITNET3B_T2048], ids=lambda c: c.name)
 def test_full_size_prefill_sampled_rows(gqa, cfg):
     q, k, v = si.prefill_config_inputs(cfg)
     print("prefill", cfg.name, flush=True)
@@ -53,14 +53,14 @@ def test_full_size_prefill_sampled_rows(gqa, cfg):
 
 @pytest.fixture(scope="module")
 def decode_data():
-    cfg = si.C5_DECODE_N1
+    cfg = si.DECODE_L32768_N1
     print("generating the decode cache (2 x %.1f GiB)" % (cfg.kv_bytes() / 2 / 2**30), flush=True)
     _, kc, vc = si.decode_inputs(cfg.B, 1, cfg.Hq, cfg.Hkv, cfg.total_len, cfg.d, cfg.dtype, cfg.seed,
                                  device="cuda")
     return kc, vc
 
 
-@pytest.mark.parametrize("cfg", [si.C5_DECODE_N1, si.C5_DECODE_N4], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [si.DECODE_L32768_N1, si.DECODE_L32768_N4], ids=lambda c: c.name)
 def test_full_size_decode_sampled_units(gqa, decode_data, cfg):
     kc, vc = decode_data  # the cache does not depend on newTokens
     q = si.decode_query(cfg.B, cfg.n, cfg.Hq, cfg.d, cfg.dtype, cfg.seed)
@@ -82,7 +82,7 @@ def test_full_size_decode_sampled_units(gqa, decode_data, cfg):
     assert worst <= TOL[cfg.dtype], worst
 
 
-@pytest.mark.parametrize("cfg", [si.C5_DECODE_N1, si.C5_DECODE_N4], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [si.DECODE_L32768_N1, si.DECODE_L32768_N4], ids=lambda c: c.name)
 def test_full_size_paged_decode(gqa, decode_data, cfg):
     """The same cache scattered into 16-position blocks in a random order: attn_decode_paged
     must give exactly attn_decode_cached's result (same kernels and split plan), and match

@@ -11,7 +11,7 @@ The cache is written in its dtype, so the bar is the rounding of that dtype:
   4 * 2^-24 * (|k1| + |k2|) for the pair (k1, k2) it comes from;
 * every row the call does not own keeps its bits.
 
-Positions reach 32767 (c5's history) so the angle's reduction is exercised; head dims
+Positions reach 32767 (the long decode history) so the angle's reduction is exercised; head dims
 64, 80 (the BitNet-3B shape) and 128; float32 and bf16 caches; paged pools with blocks
 in random order, and sequences whose metadata does not fit are left unwritten.
 """

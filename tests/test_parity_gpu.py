@@ -67,7 +67,7 @@ def test_worked_example_prefill_and_decode(gqa):
 
 
 # ------------------------------------------------------------ small workloads
-@pytest.mark.parametrize("cfg", [si.C1_SINGLE_HEAD, si.C2_MHA_F32, si.C2_MHA_BF16], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [si.SINGLE_HEAD_T16_F32, si.MHA_T512_F32, si.MHA_T512_BF16], ids=lambda c: c.name)
 def test_small_workloads(gqa, cfg):
     q, k, v = si.prefill_config_inputs(cfg)
     want = oracle.prefill(q, k, v, cfg.scale, True)
