@@ -349,11 +349,13 @@ def attn_backward_workspace_bytes(B, Hq, Hkv, T, d, dtype=GQA_BF16) -> int:
 def attn_backward(q, k, v, out, dout, lse, scale=None, causal=True, dq=None, dk=None, dv=None,
                   workspace=None, stream=None):
     """Gradients (dq, dk, dv) float32 of <dout, attention(q, k, v)> from the forward's
-    out and lse (attn_prefill_lse); q, k, v bf16."""
+    out and lse (attn_prefill_lse); q, k, v float32 or bfloat16."""
     B, Hq, T, d = q.shape
     Hkv = k.shape[1]
     if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d or v.shape != k.shape:
         raise ValueError("k, v must be [B, Hkv, T, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
     for t, n in ((out, "out"), (dout, "dout")):
         if t.shape != q.shape or t.dtype != torch.float32:
             raise ValueError("%s must be float32 of shape %s" % (n, tuple(q.shape)))

@@ -280,8 +280,8 @@ int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool
 
 size_t attn_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d_h, int dtype) {
   if (check_common(dtype, B, Hq, Hkv, d_h) != GQA_OK || T < 0) return 0;
-  if (!gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv)) return 0;
-  return gqa::backward_workspace_bytes(B, Hq, T, d_h);
+  if (gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv)) return gqa::backward_workspace_bytes(B, Hq, T, d_h);
+  return gqa::backward_generic_workspace_bytes(B, Hq, T);
 }
 
 int attn_backward(const void* q, const void* k, const void* v, const float* out, const float* dout,
@@ -291,17 +291,20 @@ int attn_backward(const void* q, const void* k, const void* v, const float* out,
   if (rc != GQA_OK) return rc;
   if (T < 0 || !isfinite(scale) || (causal != 0 && causal != 1)) return GQA_EINVAL;
   if (T > kMaxSeq) return GQA_EUNSUPPORTED;
-  if (!gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv)) return GQA_EUNSUPPORTED;
   if (B == 0 || T == 0) return GQA_OK;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
     return GQA_EINVAL;
-  const size_t need = gqa::backward_workspace_bytes(B, Hq, T, d_h);
+  const bool mfma = gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
+  const size_t need = mfma ? gqa::backward_workspace_bytes(B, Hq, T, d_h)
+                           : gqa::backward_generic_workspace_bytes(B, Hq, T);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return GQA_EWORKSPACE;
   gqa::BackwardArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, T, d_h, scale, causal,
                       nullptr, nullptr, nullptr};
-  return status_of(gqa::launch_attn_backward_mfma(a, workspace, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(mfma ? gqa::launch_attn_backward_mfma(a, workspace, s)
+                        : gqa::launch_attn_backward_generic(a, workspace, dtype, s));
 }
 
 int attn_kv_append(const float* k_new, const float* v_new, void* kcache, void* vcache,

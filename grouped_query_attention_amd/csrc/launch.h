@@ -125,5 +125,8 @@ struct BackwardArgs {
 };
 size_t backward_workspace_bytes(int B, int Hq, int T, int d);
 hipError_t launch_attn_backward_mfma(BackwardArgs a, void* workspace, hipStream_t stream);
+// Vector-ALU backward: fp32 or bf16 (dtype), any d <= 256; lse2 and Dv in the workspace.
+size_t backward_generic_workspace_bytes(int B, int Hq, int T);
+hipError_t launch_attn_backward_generic(BackwardArgs a, void* workspace, int dtype, hipStream_t stream);
 
 }  // namespace gqa

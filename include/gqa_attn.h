@@ -227,12 +227,12 @@ int attn_prefill_lse(const void* q, const void* k, const void* v, float* out, fl
  *   dk [B,Hkv,T,d_h] = scale * sum over the group's query heads and rows of dS_ij q_i
  *   dv [B,Hkv,T,d_h] = sum over the group's query heads and rows of P_ij dout_i
  * with P_ij = exp(s_ij - lse_i), dS_ij = P_ij (dout_i . v_j - dout_i . out_i).
- *   q, k, v  bf16, as the forward;  out, dout, lse, dq, dk, dv float32
+ *   q, k, v  of dtype, as the forward;  out, dout, lse, dq, dk, dv float32
  *   workspace: device memory of attn_backward_workspace_bytes(...) bytes, 256-byte aligned
- *   (dout rounded to bf16 for the matrix cores, and two float32 statistics per row)
- * Built for dtype GQA_BF16 with d_h a multiple of 16, at most 128 (GQA_EUNSUPPORTED
- * otherwise; the workspace query then returns 0).  Errors as attn_prefill, plus
- * GQA_EWORKSPACE.  The result is deterministic (no atomics).
+ *   (two float32 statistics per row, and for the matrix-core path dout rounded to bf16)
+ * bf16 with d_h a multiple of 16 up to 128 runs on the matrix cores; fp32 inputs and other
+ * head dims up to 256 run on the vector ALU (fp32 throughout).  Errors as attn_prefill,
+ * plus GQA_EWORKSPACE.  The result is deterministic (no atomics).
  */
 size_t attn_backward_workspace_bytes(int B, int Hq, int Hkv, int T, int d_h, int dtype);
 int attn_backward(const void* q, const void* k, const void* v, const float* out, const float* dout,
