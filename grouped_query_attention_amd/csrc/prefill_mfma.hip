@@ -20,17 +20,21 @@
 //    which is a valid K-ordering as long as the A operand (V^T) uses the same one.
 //    ds_read_b64_tr_b16 reads four consecutive keys of one head-dim column out of the
 //    row-major V tile, so V never needs a transposed copy.
-//  * Online softmax in log2 units (scale*log2(e) folded into one FMA before
-//    v_exp_f32); the running max is only moved when it grows by more than 8, so the
-//    O rescale is skipped on almost every tile (values of p stay below 2^8).
+//  * Online softmax in log2 units over 32-key blocks (scale*log2(e) folded into one
+//    FMA before v_exp_f32); the running max is only moved when a block's max exceeds it
+//    by more than 8, so the O rescale is skipped on almost every block (p stays below
+//    2^8).
 //  * K/V rows go from HBM straight into LDS (global_load_lds_dwordx4, no register
-//    staging) in stages of 128 keys, double-buffered in two separate LDS arrays; the
-//    next stage's loads are issued once the current stage's last LDS reads are out.
-//  * Causal skipping: 64-key tiles entirely above a wave's diagonal are not computed;
-//    the mask is only evaluated on diagonal tiles.  A local window (the multi-query
+//    staging) in stages of 128 keys, double-buffered in two separate LDS arrays; stage
+//    t+1's loads are in flight during all of stage t.
+//  * A stage fully visible to every row of a wave runs as a software pipeline over its
+//    four blocks: the softmax of block b (vector ALU) beside the S^T of block b+1 and
+//    the P V of block b-1 (matrix core), interleaved by sched_group_barrier.
+//  * Causal skipping: 32-key blocks entirely above a wave's diagonal are not computed;
+//    the mask is only evaluated on diagonal blocks.  A local window (the multi-query
 //    primer's local attention, section 4.1: keys p-W+1 .. p) skips from both sides:
-//    stages below the workgroup's first window start are never loaded, tiles below a
-//    wave's window are not computed, and window-edge tiles are masked.
+//    stages below the workgroup's first window start are never loaded, blocks below a
+//    wave's window are not computed, and window-edge blocks are masked.
 //  * Heaviest q-tiles are dispatched first; blocks of one (batch, head group) keep
 //    the same block-id residue mod 8, i.e. stay on one XCD and share its L2.
 #include <hip/hip_runtime.h>
