@@ -56,32 +56,66 @@ struct BGeo {
   static constexpr int RS = 2 * D + 16;
 };
 
+// Tiles read both ways (TS stride) are swizzled: the 16-byte chunk c of row r is stored
+// in chunk slot c ^ ((r >> 2) & 3) of that row.  With TS = 64 mod 256 (or 192), four
+// consecutive rows already fall in the four 64-byte quarters of the 256-byte bank
+// window, which is what the transposed reads need; the swizzle additionally spreads the
+// 16 rows that one ds_read_b128 pass serves over 16 distinct chunks, so the row reads
+// are conflict-free too.  TS / 16 is a multiple of 4, so a swizzled slot stays inside
+// its row.
+
+// Row fragment for MFMA step st of a row `r` (16-byte chunk 2*st + half of the row) in
+// a swizzled tile: chunk (2st + half) ^ g with g = (r >> 2) & 3 sits at
+// 32*(st ^ (g >> 1)) + 16*(half ^ (g & 1)), i.e. at `even + 32*st` for even st and
+// `odd + 32*st` for odd st.
+struct SwzRow {
+  const char* even;
+  const char* odd;
+  __device__ __forceinline__ SwzRow(const char* row_start, int r, int half) {
+    const int g = (r >> 2) & 3;
+    const char* b = row_start + 16 * (half ^ (g & 1));
+    even = b + 32 * (g >> 1);
+    odd = b - 32 * (g >> 1);
+  }
+  __device__ __forceinline__ bf16x8 frag(int st) const {
+    return *reinterpret_cast<const bf16x8*>((st & 1 ? odd : even) + 32 * st);
+  }
+};
+
 __device__ __forceinline__ bf16x8 ld_row_frag(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // transposed fragment: lane (16-lane group g, slot s) gets head dim m0 + s of the 8 rows
 // {4h..4h+3, 8+4h..8+4h+3} + r0 (h = lane / 32) -- the K-ordering of the bf16
-// accumulator operands.  `tile` is the first row of the 16-row step, `db` the 32-dim block.
+// accumulator operands.  `tile` is the first row of the 16-row step (a multiple of 16
+// rows into a swizzled tile), `db` the 32-dim block.  The lane's 8 bytes lie in chunk
+// 4*db + 2*(g & 1) + ((s >> 1) & 1) of its row; rows 4h.. have swizzle h, rows 8+4h.. h+2.
 template <int TS>
 __device__ __forceinline__ bf16x8 ld_tr_frag(const char* tile, int lane, int db) {
   const int grp = lane >> 4, sl = lane & 15, half = lane >> 5;
-  const char* p = tile + (4 * half + (sl >> 2)) * TS + (16 * (grp & 1) + 4 * (sl & 3)) * 2 + db * 64;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * TS));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  const int c0 = ((sl >> 1) & 1) ^ half;  // low chunk bit after the swizzle (both reads)
+  const int in8 = 8 * (sl & 1);
+  const char* lo = tile + (4 * half + (sl >> 2)) * TS + 16 * (2 * (grp & 1) + c0) + in8 + db * 64;
+  const char* hi = tile + (8 + 4 * half + (sl >> 2)) * TS + 16 * (2 * ((grp & 1) ^ 1) + c0) + in8 + db * 64;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lo);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Direct global->LDS copy of `rows` rows of `D` bf16 (row i at src + i*D, rows past
-// `valid` read row valid-1) into a tile of row stride `stride` bytes.  Spread over the
-// `nwaves` waves of the workgroup; each wave instruction fills 64 16-byte slots.
-template <int D>
+// `valid` read row valid-1) into a tile of row stride `stride` bytes, swizzled as above
+// when SWZ.  Spread over the `nwaves` waves of the workgroup; each wave instruction fills
+// 64 16-byte slots (slot cc of row r receives chunk cc ^ swizzle; padding slots read
+// chunk 0 and are never used).
+template <int D, bool SWZ>
 __device__ __forceinline__ void stage_rows(const uint16_t* src, int valid, char* dst, int stride, int rows,
                                            int wave, int nwaves, int lane) {
   const int P = stride / 16, C16 = D / 8;
   const int n_inst = rows * P / 64;
   for (int inst = wave; inst < n_inst; inst += nwaves) {
     const int p = inst * 64 + lane, r = p / P, cc = p % P;
+    const int lc = SWZ ? (cc ^ ((r >> 2) & 3)) : cc;
     const int rr = r < valid ? r : valid - 1;
-    const char* s = reinterpret_cast<const char*>(src) + (long long)rr * D * 2 + (cc < C16 ? cc : 0) * 16;
+    const char* s = reinterpret_cast<const char*>(src) + (long long)rr * D * 2 + (lc < C16 ? lc : 0) * 16;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)s,
                                      (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
   }
@@ -172,8 +206,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const int r0 = (qs0 + si % per_head) * kQStage;
     const long long rowbase = ((long long)b * Hq + hq) * T + r0;
     const int valid = T - r0;
-    stage_rows<D>(q + rowbase * D, valid, buf, TS, kQStage, wave, kKvWaves, lane);
-    stage_rows<D>(dob + rowbase * D, valid, buf + kTile, TS, kQStage, wave, kKvWaves, lane);
+    stage_rows<D, true>(q + rowbase * D, valid, buf, TS, kQStage, wave, kKvWaves, lane);
+    stage_rows<D, true>(dob + rowbase * D, valid, buf + kTile, TS, kQStage, wave, kKvWaves, lane);
     // lse2 and D of the 64 rows: one wave instruction each (4 bytes per lane)
     if (wave == 0 || wave == 1) {
       const float* srcf = (wave == 0 ? lse2 : Dv) + rowbase + min(lane, valid - 1);
@@ -199,12 +233,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       // S = Q K^T and dP = dO V^T: accumulator r holds query row 8*(r/4)+4*half+r%4 of
       // the block, key `key`
       f32x16 s = f32x16{}, dp = f32x16{};
-      const char* qrow = qt + (32 * blk + col) * TS + half * 16;
-      const char* orow = ot + (32 * blk + col) * TS + half * 16;
+      const SwzRow qrow(qt + (32 * blk + col) * TS, col, half);
+      const SwzRow orow(ot + (32 * blk + col) * TS, col, half);
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(qrow + st * 32), kf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(orow + st * 32), vf[st], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qrow.frag(st), kf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(orow.frag(st), vf[st], dp, 0, 0, 0);
       }
       // P = 2^(s*c - lse2), dS = P (dP - D); masked entries are exact zeros
       bf16x8 pb[2], sb[2];
@@ -249,12 +283,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16{};
       dp[blk] = f32x16{};
-      const char* qrow = qt + (32 * blk + col) * TS + half * 16;
-      const char* orow = ot + (32 * blk + col) * TS + half * 16;
+      const SwzRow qrow(qt + (32 * blk + col) * TS, col, half);
+      const SwzRow orow(ot + (32 * blk + col) * TS, col, half);
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(qrow + st * 32), kf[st], s[blk], 0, 0, 0);
-        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(orow + st * 32), vf[st], dp[blk], 0, 0, 0);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qrow.frag(st), kf[st], s[blk], 0, 0, 0);
+        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(orow.frag(st), vf[st], dp[blk], 0, 0, 0);
       }
     }
     bf16x8 pb[2][2], sb[2][2];
@@ -388,8 +422,8 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
   const int nstages = (kend + kKStage - 1) / kKStage;
   auto stage = [&](int t, char* buf) __attribute__((always_inline)) {
     const int r0 = t * kKStage;
-    stage_rows<D>(k + (kvb + r0) * D, T - r0, buf, TS, kKStage, wave, kQWaves, lane);
-    stage_rows<D>(v + (kvb + r0) * D, T - r0, buf + kKT, RS, kKStage, wave, kQWaves, lane);
+    stage_rows<D, true>(k + (kvb + r0) * D, T - r0, buf, TS, kKStage, wave, kQWaves, lane);
+    stage_rows<D, false>(v + (kvb + r0) * D, T - r0, buf + kKT, RS, kKStage, wave, kQWaves, lane);
   };
   auto compute = [&](int t, const char* buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -400,11 +434,11 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
       // S^T = K Q^T and dP^T = V dO^T: accumulator r holds key 8*(r/4)+4*half+r%4 of the
       // block, query qi
       f32x16 s = f32x16{}, dp = f32x16{};
-      const char* krow = buf + (32 * blk + col) * TS + half * 16;
+      const SwzRow krow(buf + (32 * blk + col) * TS, col, half);
       const char* vrow = buf + kKT + (32 * blk + col) * RS + half * 16;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(krow + st * 32), qf[st], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(krow.frag(st), qf[st], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(vrow + st * 32), of[st], dp, 0, 0, 0);
       }
       bf16x8 sb[2];
@@ -438,11 +472,11 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16{};
       dp[blk] = f32x16{};
-      const char* krow = buf + (32 * blk + col) * TS + half * 16;
+      const SwzRow krow(buf + (32 * blk + col) * TS, col, half);
       const char* vrow = buf + kKT + (32 * blk + col) * RS + half * 16;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(krow + st * 32), qf[st], s[blk], 0, 0, 0);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(krow.frag(st), qf[st], s[blk], 0, 0, 0);
         dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(vrow + st * 32), of[st], dp[blk], 0, 0, 0);
       }
     }
