@@ -13,7 +13,7 @@
 //
 // Three kernels, no atomics (results are deterministic):
 //  * bwd_prep_kernel: per row, D_i in fp32 from the fp32 dO and O, dO rounded to bf16
-//    for the matrix cores, lse converted to log2 units.
+//    for the matrix cores, lse converted to log2 units (HBM-bound: 16-byte loads).
 //  * bwd_dkdv_kernel: key-parallel.  A wave owns 32 keys of one K/V head (K^T and V^T
 //    fragments in registers) and walks the query blocks of every query head of its
 //    group.  Scores are formed as S = Q K^T, so each lane holds 16 queries of ONE key:
@@ -122,22 +122,27 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src, int valid, char*
 }
 
 // ---------------------------------------------------------------------------------
+// One row per group of 2^lpr_log2 lanes (the power of two at or above d/4), four
+// consecutive elements per lane: 16-byte loads of dO and O, an 8-byte store of the bf16
+// dO, the row sum reduced over the group.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ out, const float* __restrict__ dout,
                                                        const float* __restrict__ lse, uint16_t* __restrict__ dob,
                                                        float* __restrict__ lse2, float* __restrict__ Dv,
-                                                       long long rows, int d) {
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+                                                       long long rows, int d, int lpr_log2) {
+  const int lpr = 1 << lpr_log2;
+  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) >> lpr_log2;
+  const int e = 4 * (threadIdx.x & (lpr - 1));
   float acc = 0.f;
-  for (int e = lane; e < d; e += 64) {
-    const float g = dout[row * d + e];
-    acc += g * out[row * d + e];
-    dob[row * d + e] = __builtin_bit_cast(uint16_t, (__bf16)g);
+  if (row < rows && e < d) {
+    const f32x4 g = *reinterpret_cast<const f32x4*>(dout + row * d + e);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(out + row * d + e);
+    acc = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
+    const bf16x4 b = {(__bf16)g[0], (__bf16)g[1], (__bf16)g[2], (__bf16)g[3]};
+    *reinterpret_cast<bf16x4*>(dob + row * d + e) = b;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) {
+  for (int off = lpr >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && e == 0) {
     Dv[row] = acc;
     lse2[row] = lse[row] * kLog2e;
   }
@@ -589,10 +594,13 @@ hipError_t launch_attn_backward_mfma(BackwardArgs a, void* workspace, hipStream_
   a.dob = reinterpret_cast<uint16_t*>(ws);
   a.lse2 = reinterpret_cast<float*>(ws + ob);
   a.Dv = reinterpret_cast<float*>(ws + ob + fb);
-  const long long pb = (rows + 3) / 4;
+  // lanes per row: the power of two at or above d/4 (d is a multiple of 16, at most 128)
+  int lpr_log2 = 0;
+  while ((1 << lpr_log2) * 4 < a.d) ++lpr_log2;
+  const long long pb = ((rows << lpr_log2) + 255) / 256;
   if (pb > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)pb), dim3(256), 0, stream, a.out, a.dout, a.lse,
-                     a.dob, a.lse2, a.Dv, rows, a.d);
+                     a.dob, a.lse2, a.Dv, rows, a.d, lpr_log2);
   switch (a.d) {
     case 16: return launch_d<16>(a, stream);
     case 32: return launch_d<32>(a, stream);
