@@ -101,25 +101,46 @@ __device__ __forceinline__ bf16x8 ld_tr_frag(const char* tile, int lane, int db)
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Direct global->LDS copy of `rows` rows of `D` bf16 (row i at src + i*D, rows past
-// `valid` read row valid-1) into a tile of row stride `stride` bytes, swizzled as above
-// when SWZ.  Spread over the `nwaves` waves of the workgroup; each wave instruction fills
-// 64 16-byte slots (slot cc of row r receives chunk cc ^ swizzle; padding slots read
-// chunk 0 and are never used).
-template <int D, bool SWZ>
-__device__ __forceinline__ void stage_rows(const uint16_t* src, int valid, char* dst, int stride, int rows,
-                                           int wave, int nwaves, int lane) {
-  const int P = stride / 16, C16 = D / 8;
-  const int n_inst = rows * P / 64;
-  for (int inst = wave; inst < n_inst; inst += nwaves) {
-    const int p = inst * 64 + lane, r = p / P, cc = p % P;
-    const int lc = SWZ ? (cc ^ ((r >> 2) & 3)) : cc;
-    const int rr = r < valid ? r : valid - 1;
-    const char* s = reinterpret_cast<const char*>(src) + (long long)rr * D * 2 + (lc < C16 ? lc : 0) * 16;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)s,
-                                     (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
+// Direct global->LDS loads of a 64-row tile of `D` bf16 per row (row i at src + i*2D
+// bytes) into LDS rows of STRIDE bytes, swizzled as above when SWZ.  Each wave
+// instruction fills 64 consecutive 16-byte slots; slot p is row p / P, chunk slot p % P
+// (P = STRIDE / 16), which receives chunk (p % P) ^ swizzle of its row (padding slots
+// re-read chunk 0 and are never used).  A lane's source offset within a tile is the
+// same for every tile, so it is computed once per wave instruction.  In a ragged tile,
+// rows at or past `valid` re-read row valid-1.
+template <int D, int STRIDE, int NW, bool SWZ>
+struct TileLoader {
+  static constexpr int P = STRIDE / 16, C16 = D / 8, RB = 2 * D;
+  static constexpr int NI = P;                   // wave instructions per 64-row tile
+  static constexpr int I = (NI + NW - 1) / NW;   // of which this wave issues at most I
+  int off[I];
+  int wave_u;
+  __device__ __forceinline__ TileLoader(int wave, int lane) {
+    wave_u = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const int p = (wave + NW * i) * 64 + lane, r = p / P, cc = p % P;
+      const int lc = SWZ ? (cc ^ ((r >> 2) & 3)) : cc;
+      off[i] = r * RB + (lc < C16 ? lc : 0) * 16;
+    }
   }
-}
+  __device__ __forceinline__ void load(const uint16_t* src, char* dst, int valid) const {
+    const char* s = reinterpret_cast<const char*>(src);
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const int inst = wave_u + NW * i;
+      if (inst < NI) {
+        int o = off[i];
+        if (valid < 64) {
+          const int r = o / RB;
+          if (r >= valid) o -= (r - valid + 1) * RB;
+        }
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(s + o),
+                                         (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------------
 // One row per group of 2^lpr_log2 lanes (the power of two at or above d/4), four
@@ -152,6 +173,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 constexpr int kKvWaves = 4;    // waves per dK/dV workgroup, 32 keys each
 constexpr int kKvKeys = 32 * kKvWaves;
 constexpr int kQStage = 64;    // query rows per stage of the dK/dV kernel
+static_assert(kQStage == 64, "TileLoader stages 64-row tiles");
 
 template <int D>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
@@ -206,13 +228,14 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   const int nqs = (T + kQStage - 1) / kQStage;
   const int per_head = nqs - qs0;
   const int nstages = per_head * G_;
+  const TileLoader<D, TS, kKvWaves, true> ld(wave, lane);
   auto stage = [&](int si, char* buf) __attribute__((always_inline)) {
     const int hq = g * G_ + si / per_head;
     const int r0 = (qs0 + si % per_head) * kQStage;
     const long long rowbase = ((long long)b * Hq + hq) * T + r0;
     const int valid = T - r0;
-    stage_rows<D, true>(q + rowbase * D, valid, buf, TS, kQStage, wave, kKvWaves, lane);
-    stage_rows<D, true>(dob + rowbase * D, valid, buf + kTile, TS, kQStage, wave, kKvWaves, lane);
+    ld.load(q + rowbase * D, buf, valid);
+    ld.load(dob + rowbase * D, buf + kTile, valid);
     // lse2 and D of the 64 rows: one wave instruction each (4 bytes per lane)
     if (wave == 0 || wave == 1) {
       const float* srcf = (wave == 0 ? lse2 : Dv) + rowbase + min(lane, valid - 1);
@@ -374,6 +397,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------------
 constexpr int kQWaves = 8;     // waves per dQ workgroup, 32 query rows each
 constexpr int kKStage = 64;    // keys per stage of the dQ kernel
+static_assert(kKStage == 64, "TileLoader stages 64-row tiles");
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
@@ -425,10 +449,12 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
   const long long kvb = ((long long)b * Hkv + g) * (long long)T;
   const int kend = causal ? min(T, q0 + QT) : T;
   const int nstages = (kend + kKStage - 1) / kKStage;
+  const TileLoader<D, TS, kQWaves, true> ldk(wave, lane);
+  const TileLoader<D, RS, kQWaves, false> ldv(wave, lane);
   auto stage = [&](int t, char* buf) __attribute__((always_inline)) {
     const int r0 = t * kKStage;
-    stage_rows<D, true>(k + (kvb + r0) * D, T - r0, buf, TS, kKStage, wave, kQWaves, lane);
-    stage_rows<D, false>(v + (kvb + r0) * D, T - r0, buf + kKT, RS, kKStage, wave, kQWaves, lane);
+    ldk.load(k + (kvb + r0) * D, buf, T - r0);
+    ldv.load(v + (kvb + r0) * D, buf + kKT, T - r0);
   };
   auto compute = [&](int t, const char* buf) __attribute__((always_inline)) {
 #pragma unroll
