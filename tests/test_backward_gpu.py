@@ -4,8 +4,8 @@ against the float64 oracle (oracle/backward.py).
 * lse from both forward kernels (bf16 matrix cores and the fp32 vector kernel) against
   the oracle's row log-sum-exp; the output is bitwise that of attn_prefill.
 * dq, dk, dv element by element against the oracle on ragged shapes (T not a multiple
-  of the 32/64/128-row tiles), head dims 32..128 including 80, group sizes 1, 2, 4,
-  causal and not, and at the full GQA prefill workload on sampled head groups.
+  of the 32/64/128-row tiles), every head dim the matrix-core path takes (16..128 in
+  steps of 16), group sizes 1, 2, 4, causal and not, and at the full GQA prefill workload on sampled head groups.
   The GPU recomputes P from bf16 Q/K, rounds P, dS and dO to bf16 for the matrix cores
   and accumulates in fp32; the bar is the bf16-input tolerance 1.5e-2 applied to the
   gradient scaled by its own size: max|gpu - ref| <= 1.5e-2 * max(1, max|ref|).
@@ -88,6 +88,9 @@ CASES = [
     (1, 2, 1, 45, 16, True),
     (1, 16, 8, 512, 128, True),
     (1, 2, 2, 1, 64, True),
+    (1, 4, 2, 150, 48, True),
+    (2, 2, 1, 97, 96, False),
+    (1, 4, 2, 222, 112, True),
 ]
 
 
