@@ -46,8 +46,9 @@ template <int D>
 struct BGeo {
   static constexpr int KS = D / 16;           // K-steps over the head dim
   static constexpr int DB = (D + 31) / 32;    // 32-row blocks of a transposed accumulator
-  // row stride read both as 16-byte rows and transposed: 64 or 192 mod 256 bytes keeps
-  // the transposed reads conflict-free (rows up to the next 32 head dims are read)
+  // Row stride of a tile read both as 16-byte rows and transposed: 64 or 192 mod 256
+  // bytes (rows up to the next 32 head dims are read), with which four consecutive rows
+  // fall in the four 64-byte quarters of the 256-byte bank window
   static constexpr int kRead = 64 * DB;
   static constexpr int TS = (kRead % 256 <= 64) ? kRead - kRead % 256 + 64
                             : (kRead % 256 <= 192) ? kRead - kRead % 256 + 192
@@ -57,15 +58,17 @@ struct BGeo {
 };
 
 // Tiles read both ways (TS stride) are swizzled: the 16-byte chunk c of row r is stored
-// in chunk slot c ^ ((r >> 2) & 3) of that row.  With TS = 64 mod 256 (or 192), four
-// consecutive rows already fall in the four 64-byte quarters of the 256-byte bank
-// window, which is what the transposed reads need; the swizzle additionally spreads the
-// 16 rows that one ds_read_b128 pass serves over 16 distinct chunks, so the row reads
-// are conflict-free too.  TS / 16 is a multiple of 4, so a swizzled slot stays inside
-// its row.
+// in chunk slot c ^ ((r >> 2) & 3) of that row.  The 64 banks x 4 bytes of LDS serve a
+// ds_read_b128 16 lanes (16 rows of one chunk) at a time and a ds_read_b64_tr_b16 32
+// lanes (4 rows x 64 bytes) at a time.  The stride already puts rows r..r+3 in the four
+// 64-byte quarters of the bank window, which is what the transposed reads need; the
+// swizzle spreads the 16 rows of a row pass over 16 distinct chunks.  TS / 16 is a
+// multiple of 4, so a swizzled slot stays inside its row.  (An unpadded 256-byte row
+// for d = 128 with a two-level swizzle, conflict-free as well, measured slower.)
+__device__ __forceinline__ int swz(int c, int r) { return c ^ ((r >> 2) & 3); }
 
-// Row fragment for MFMA step st of a row `r` (16-byte chunk 2*st + half of the row) in
-// a swizzled tile: chunk (2st + half) ^ g with g = (r >> 2) & 3 sits at
+// Row fragment for MFMA step st of row r (16-byte chunk 2*st + half of the row) in a
+// swizzled tile: chunk (2st + half) ^ g with g = (r >> 2) & 3 sits at
 // 32*(st ^ (g >> 1)) + 16*(half ^ (g & 1)), i.e. at `even + 32*st` for even st and
 // `odd + 32*st` for odd st.
 struct SwzRow {
@@ -88,30 +91,33 @@ __device__ __forceinline__ bf16x8 ld_row_frag(const char* p) { return *reinterpr
 // {4h..4h+3, 8+4h..8+4h+3} + r0 (h = lane / 32) -- the K-ordering of the bf16
 // accumulator operands.  `tile` is the first row of the 16-row step (a multiple of 16
 // rows into a swizzled tile), `db` the 32-dim block.  The lane's 8 bytes lie in chunk
-// 4*db + 2*(g & 1) + ((s >> 1) & 1) of its row; rows 4h.. have swizzle h, rows 8+4h.. h+2.
-template <int TS>
+// 4*db + 2*(g & 1) + ((s >> 1) & 1) of its row.
+template <int D>
 __device__ __forceinline__ bf16x8 ld_tr_frag(const char* tile, int lane, int db) {
+  constexpr int TS = BGeo<D>::TS;
   const int grp = lane >> 4, sl = lane & 15, half = lane >> 5;
-  const int c0 = ((sl >> 1) & 1) ^ half;  // low chunk bit after the swizzle (both reads)
+  const int c = 4 * db + 2 * (grp & 1) + ((sl >> 1) & 1);
   const int in8 = 8 * (sl & 1);
-  const char* lo = tile + (4 * half + (sl >> 2)) * TS + 16 * (2 * (grp & 1) + c0) + in8 + db * 64;
-  const char* hi = tile + (8 + 4 * half + (sl >> 2)) * TS + 16 * (2 * ((grp & 1) ^ 1) + c0) + in8 + db * 64;
+  const int rlo = 4 * half + (sl >> 2), rhi = rlo + 8;
+  const char* lo = tile + rlo * TS + 16 * swz(c, rlo) + in8;
+  const char* hi = tile + rhi * TS + 16 * swz(c, rhi) + in8;
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lo);
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)hi);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Direct global->LDS loads of a 64-row tile of `D` bf16 per row (row i at src + i*2D
+// Direct global->LDS loads of a ROWS-row tile of `D` bf16 per row (row i at src + i*2D
 // bytes) into LDS rows of STRIDE bytes, swizzled as above when SWZ.  Each wave
 // instruction fills 64 consecutive 16-byte slots; slot p is row p / P, chunk slot p % P
-// (P = STRIDE / 16), which receives chunk (p % P) ^ swizzle of its row (padding slots
-// re-read chunk 0 and are never used).  A lane's source offset within a tile is the
-// same for every tile, so it is computed once per wave instruction.  In a ragged tile,
-// rows at or past `valid` re-read row valid-1.
-template <int D, int STRIDE, int NW, bool SWZ>
+// (P = STRIDE / 16), which receives chunk swz(p % P) of its row (padding slots re-read
+// chunk 0 and are never used).  A lane's source offset within a tile is the same for
+// every tile, so it is computed once per wave instruction.  In a ragged tile, rows at
+// or past `valid` re-read row valid-1.
+template <int D, int STRIDE, int ROWS, int NW, bool SWZ>
 struct TileLoader {
   static constexpr int P = STRIDE / 16, C16 = D / 8, RB = 2 * D;
-  static constexpr int NI = P;                   // wave instructions per 64-row tile
+  static_assert(ROWS * P % 64 == 0, "a tile is a whole number of wave instructions");
+  static constexpr int NI = ROWS * P / 64;       // wave instructions per tile
   static constexpr int I = (NI + NW - 1) / NW;   // of which this wave issues at most I
   int off[I];
   int wave_u;
@@ -120,7 +126,7 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < I; ++i) {
       const int p = (wave + NW * i) * 64 + lane, r = p / P, cc = p % P;
-      const int lc = SWZ ? (cc ^ ((r >> 2) & 3)) : cc;
+      const int lc = SWZ ? swz(cc, r) : cc;
       off[i] = r * RB + (lc < C16 ? lc : 0) * 16;
     }
   }
@@ -131,7 +137,7 @@ struct TileLoader {
       const int inst = wave_u + NW * i;
       if (inst < NI) {
         int o = off[i];
-        if (valid < 64) {
+        if (valid < ROWS) {
           const int r = o / RB;
           if (r >= valid) o -= (r - valid + 1) * RB;
         }
@@ -173,7 +179,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 constexpr int kKvWaves = 4;    // waves per dK/dV workgroup, 32 keys each
 constexpr int kKvKeys = 32 * kKvWaves;
 constexpr int kQStage = 64;    // query rows per stage of the dK/dV kernel
-static_assert(kQStage == 64, "TileLoader stages 64-row tiles");
 
 template <int D>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
@@ -183,8 +188,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     int n_kb) {
   using G = BGeo<D>;
   constexpr int KS = G::KS, DB = G::DB, TS = G::TS;
-  constexpr int kTile = kQStage * TS;
-  constexpr int kBuf = 2 * kTile + 2 * kQStage * 4;  // Q tile, dO tile, lse2, D
+  constexpr int QS = kQStage;              // query rows per stage
+  constexpr int NBLK = QS / 32;            // 32-row blocks per stage
+  constexpr int kTile = QS * TS;
+  constexpr int kPer = (QS + 63) / 64;  // wave instructions per row statistic
+  constexpr int kBuf = 2 * kTile + 2 * kPer * 256;  // Q tile, dO tile, lse2, D
   __shared__ __attribute__((aligned(16))) char lds_a[kBuf];
   __shared__ __attribute__((aligned(16))) char lds_b[kBuf];
 
@@ -222,131 +230,128 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     dva[db] = f32x16{};
   }
 
-  // query stages: (query head, 64-row block), for every head of the group; causally the
-  // rows before the workgroup's first key see none of its keys
-  const int qs0 = causal ? k0 / kQStage : 0;
-  const int nqs = (T + kQStage - 1) / kQStage;
+  // query stages: (query head, QS-row block), for every head of the group; causally the
+  // rows before the workgroup's first key see none of its keys (k0 is a multiple of QS)
+  const int qs0 = causal ? k0 / QS : 0;
+  const int nqs = (T + QS - 1) / QS;
   const int per_head = nqs - qs0;
   const int nstages = per_head * G_;
-  const TileLoader<D, TS, kKvWaves, true> ld(wave, lane);
+  const TileLoader<D, TS, QS, kKvWaves, true> ld(wave, lane);
   auto stage = [&](int si, char* buf) __attribute__((always_inline)) {
     const int hq = g * G_ + si / per_head;
-    const int r0 = (qs0 + si % per_head) * kQStage;
+    const int r0 = (qs0 + si % per_head) * QS;
     const long long rowbase = ((long long)b * Hq + hq) * T + r0;
     const int valid = T - r0;
     ld.load(q + rowbase * D, buf, valid);
     ld.load(dob + rowbase * D, buf + kTile, valid);
-    // lse2 and D of the 64 rows: one wave instruction each (4 bytes per lane)
-    if (wave == 0 || wave == 1) {
-      const float* srcf = (wave == 0 ? lse2 : Dv) + rowbase + min(lane, valid - 1);
+    // lse2 and D of the QS rows: kPer wave instructions each (4 bytes per lane)
+    if (wave < 2 * kPer) {
+      const int part = wave % kPer, r = 64 * part + lane;
+      const float* srcf = (wave < kPer ? lse2 : Dv) + rowbase + min(r, valid - 1);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)srcf,
-                                       (__attribute__((address_space(3))) void*)(buf + 2 * kTile + wave * kQStage * 4),
+                                       (__attribute__((address_space(3))) void*)(buf + 2 * kTile + wave * 256),
                                        4, 0, 0);
     }
   };
 
-  auto compute = [&](int si, const char* buf) __attribute__((always_inline)) {
-    const int r0 = (qs0 + si % per_head) * kQStage;
-    const char* qt = buf;
-    const char* ot = buf + kTile;
-    const float* l2s = reinterpret_cast<const float*>(buf + 2 * kTile);
-    const float* dvs = l2s + kQStage;
+  // S = Q K^T and dP = dO V^T of 32-row block `blk` of a stage: accumulator r holds query
+  // row 8*(r/4)+4*half+r%4 of the block, key `key`
+  auto sdp = [&](const char* buf, int blk, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    const SwzRow qrow(buf + (32 * blk + col) * TS, col, half);
+    const SwzRow orow(buf + kTile + (32 * blk + col) * TS, col, half);
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-    for (int blk = 0; blk < kQStage / 32; ++blk) {
+    for (int st = 0; st < KS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qrow.frag(st), kf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(orow.frag(st), vf[st], dp, 0, 0, 0);
+    }
+    // the row fragments are read kAhead matrix ops ahead of their use (left to itself
+    // the scheduler issued each read right before its matrix op, exposing the LDS
+    // latency at one wave per SIMD)
+    constexpr int kAhead = 2 * KS < 10 ? 2 * KS : 10;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  };
+  // P = 2^(s*c - lse2) and dS = P (dP - D) in bf16; with `mask`, entries outside the
+  // causal triangle or the sequence are exact zeros (first query row of the block: i0)
+  auto soft = [&](const char* buf, int blk, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&sb)[2],
+                  bool mask, int i0) __attribute__((always_inline)) {
+    const float* l2s = reinterpret_cast<const float*>(buf + 2 * kTile);
+    const float* dvs = reinterpret_cast<const float*>(buf + 2 * kTile + kPer * 256);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);  // row within the stage
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2s[qr]));
+      if (mask) {
+        const int i = i0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool ok = i < T && key < T && (!causal || key <= i);
+        p = ok ? p : 0.f;
+      }
+      pb[r >> 3][r & 7] = (__bf16)p;
+      sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dvs[qr]));
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 query rows
+  auto grad = [&](const char* buf, int blk, const bf16x8 (&pb)[2], const bf16x8 (&sb)[2])
+                  __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const char* qt16 = buf + (32 * blk + 16 * kk) * TS;
+      const char* ot16 = buf + kTile + (32 * blk + 16 * kk) * TS;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<D>(ot16, lane, db), pb[kk], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<D>(qt16, lane, db), sb[kk], dka[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // A stage with masks: block by block (a loop, not unrolled: these stages are few),
+  // skipping blocks this wave cannot see
+  auto compute = [&](int si, const char* buf) __attribute__((always_inline)) {
+    const int r0 = (qs0 + si % per_head) * QS;
+#pragma unroll 1
+    for (int blk = 0; blk < NBLK; ++blk) {
       const int i0 = r0 + 32 * blk;  // first query row of the block
       // causal: rows before this wave's first key see none of its keys
       if (causal && i0 + 31 < kw) continue;
       if (i0 >= T) continue;
       const bool edge = (causal && i0 < kw + 31) || i0 + 32 > T || kw + 32 > T;
-      // S = Q K^T and dP = dO V^T: accumulator r holds query row 8*(r/4)+4*half+r%4 of
-      // the block, key `key`
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const SwzRow qrow(qt + (32 * blk + col) * TS, col, half);
-      const SwzRow orow(ot + (32 * blk + col) * TS, col, half);
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qrow.frag(st), kf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(orow.frag(st), vf[st], dp, 0, 0, 0);
-      }
-      // P = 2^(s*c - lse2), dS = P (dP - D); masked entries are exact zeros
+      f32x16 s, dp;
       bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);  // row within the stage
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2s[qr]));
-        if (edge) {
-          const int i = r0 + qr;
-          const bool ok = i < T && key < T && (!causal || key <= i);
-          p = ok ? p : 0.f;
-        }
-        const float ds = p * (dp[r] - dvs[qr]);
-        pb[r >> 3][r & 7] = (__bf16)p;
-        sb[r >> 3][r & 7] = (__bf16)ds;
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 query rows
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const char* ot16 = ot + (32 * blk + 16 * kk) * TS;
-        const char* qt16 = qt + (32 * blk + 16 * kk) * TS;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(ot16, lane, db), pb[kk], dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(qt16, lane, db), sb[kk], dka[db], 0, 0, 0);
-        }
-      }
+      sdp(buf, blk, s, dp);
+      soft(buf, blk, s, dp, pb, sb, edge, i0);
+      grad(buf, blk, pb, sb);
     }
   };
 
-  // A stage every row and key of which is visible to this wave (no mask): the two
-  // 32-row blocks in straight-line code, so the second block's S and dP products can
-  // run beside the first block's exp and dS vector work, and the first block's dV and
-  // dK products beside the second block's.
+  // A stage every row and key of which is visible to this wave (no mask): its 32-row
+  // blocks as one software pipeline in straight-line code -- block b+1's S and dP
+  // products, block b's exp and dS vector work and block b-1's gradient products are
+  // independent, so the matrix cores and the vector ALU overlap inside the wave.
   auto compute_fast = [&](const char* buf) __attribute__((always_inline)) {
-    const char* qt = buf;
-    const char* ot = buf + kTile;
-    const float* l2s = reinterpret_cast<const float*>(buf + 2 * kTile);
-    const float* dvs = l2s + kQStage;
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16{};
-      dp[blk] = f32x16{};
-      const SwzRow qrow(qt + (32 * blk + col) * TS, col, half);
-      const SwzRow orow(ot + (32 * blk + col) * TS, col, half);
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qrow.frag(st), kf[st], s[blk], 0, 0, 0);
-        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(orow.frag(st), vf[st], dp[blk], 0, 0, 0);
-      }
-    }
     bf16x8 pb[2][2], sb[2][2];
+    sdp(buf, 0, s[0], dp[0]);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -l2s[qr]));
-        pb[blk][r >> 3][r & 7] = (__bf16)p;
-        sb[blk][r >> 3][r & 7] = (__bf16)(p * (dp[blk][r] - dvs[qr]));
-      }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const char* ot16 = ot + (32 * blk + 16 * kk) * TS;
-        const char* qt16 = qt + (32 * blk + 16 * kk) * TS;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(ot16, lane, db), pb[blk][kk], dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(qt16, lane, db), sb[blk][kk], dka[db], 0, 0, 0);
-        }
-      }
+    for (int blk = 0; blk < NBLK; ++blk) {
+      if (blk + 1 < NBLK) sdp(buf, blk + 1, s[(blk + 1) & 1], dp[(blk + 1) & 1]);
+      soft(buf, blk, s[blk & 1], dp[blk & 1], pb[blk & 1], sb[blk & 1], false, 0);
+      if (blk >= 1) grad(buf, blk - 1, pb[(blk - 1) & 1], sb[(blk - 1) & 1]);
+    }
+    grad(buf, NBLK - 1, pb[(NBLK - 1) & 1], sb[(NBLK - 1) & 1]);
   };
   // every row of the stage is at or after this wave's last key, inside T, and every key
   // of the wave is inside T
   auto stage_interior = [&](int si) __attribute__((always_inline)) {
-    const int r0 = (qs0 + si % per_head) * kQStage;
-    return (!causal || r0 >= kw + 31) && r0 + kQStage <= T && kw + 32 <= T;
+    const int r0 = (qs0 + si % per_head) * QS;
+    return (!causal || r0 >= kw + 31) && r0 + QS <= T && kw + 32 <= T;
   };
   auto run = [&](int si, const char* buf) __attribute__((always_inline)) {
     if (stage_interior(si))
@@ -397,7 +402,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------------
 constexpr int kQWaves = 8;     // waves per dQ workgroup, 32 query rows each
 constexpr int kKStage = 64;    // keys per stage of the dQ kernel
-static_assert(kKStage == 64, "TileLoader stages 64-row tiles");
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
@@ -449,8 +453,8 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
   const long long kvb = ((long long)b * Hkv + g) * (long long)T;
   const int kend = causal ? min(T, q0 + QT) : T;
   const int nstages = (kend + kKStage - 1) / kKStage;
-  const TileLoader<D, TS, kQWaves, true> ldk(wave, lane);
-  const TileLoader<D, RS, kQWaves, false> ldv(wave, lane);
+  const TileLoader<D, TS, kKStage, kQWaves, true> ldk(wave, lane);
+  const TileLoader<D, RS, kKStage, kQWaves, false> ldv(wave, lane);
   auto stage = [&](int t, char* buf) __attribute__((always_inline)) {
     const int r0 = t * kKStage;
     ldk.load(k + (kvb + r0) * D, buf, T - r0);
@@ -489,7 +493,7 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
         const char* kt16 = buf + (32 * blk + 16 * kk) * TS;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(kt16, lane, db), sb[kk], dqa[db], 0, 0, 0);
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<D>(kt16, lane, db), sb[kk], dqa[db], 0, 0, 0);
       }
     }
   };
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
         const char* kt16 = buf + (32 * blk + 16 * kk) * TS;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<TS>(kt16, lane, db), sb[blk][kk], dqa[db], 0, 0, 0);
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<D>(kt16, lane, db), sb[blk][kk], dqa[db], 0, 0, 0);
       }
   };
   auto run = [&](int t, const char* buf) __attribute__((always_inline)) {
