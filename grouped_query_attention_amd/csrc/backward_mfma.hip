@@ -151,7 +151,7 @@ struct TileLoader {
 // ---------------------------------------------------------------------------------
 // One row per group of 2^lpr_log2 lanes (the power of two at or above d/4), four
 // consecutive elements per lane: 16-byte loads of dO and O, an 8-byte store of the bf16
-// dO, the row sum reduced over the group.
+// dO, the row sum reduced over the group.  dO and O are read once: non-temporal loads.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ out, const float* __restrict__ dout,
                                                        const float* __restrict__ lse, uint16_t* __restrict__ dob,
@@ -162,8 +162,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   const int e = 4 * (threadIdx.x & (lpr - 1));
   float acc = 0.f;
   if (row < rows && e < d) {
-    const f32x4 g = *reinterpret_cast<const f32x4*>(dout + row * d + e);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(out + row * d + e);
+    const f32x4 g = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dout + row * d + e));
+    const f32x4 o = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(out + row * d + e));
     acc = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
     const bf16x4 b = {(__bf16)g[0], (__bf16)g[1], (__bf16)g[2], (__bf16)g[3]};
     *reinterpret_cast<bf16x4*>(dob + row * d + e) = b;
