@@ -41,7 +41,13 @@ constexpr int kWaves = 4;        // independent waves per workgroup
 constexpr int kTile = 32;        // keys per tile
 constexpr int kCols = 16;        // query columns per MFMA tile
 constexpr float kLazyTau = 8.f;  // log2 growth of the running max tolerated before rescale
-constexpr int kTargetWaves = 8192;
+// Split target: two waves per SIMD (256 CUs x 4 SIMDs).  Every wave of a launch walks a
+// chunk of the same length, so a wave count that is not a whole multiple of the SIMD
+// count leaves a partial last round (1536 waves for the 64 x 8 KV heads of a 32768-key
+// history ran at 5.8 TB/s, 2048 at 7.0).  Longer chunks also mean fewer partials to merge:
+// 8192 waves ran at 6.6 TB/s, 4096 at 6.9.
+constexpr int kSimds = 1024;
+constexpr int kTargetWaves = 2 * kSimds;
 
 template <int D>
 struct DGeo {
@@ -445,9 +451,16 @@ int decode_key_span(int len, int n, int window) {
   return span < len ? (int)span : len;
 }
 
-// Pure function of the shape: enough chunks that the launch has ~kTargetWaves waves,
-// each chunk a multiple of the 32-key tile; partials are (d + 2) floats per chunk,
-// query row and head.  `total_len` is the most keys one sequence walks.
+// Share of the SIMDs busy over the rounds a launch of `waves` equal waves needs
+static double simd_fill(long long waves) {
+  const long long rounds = (waves + kSimds - 1) / kSimds;
+  return (double)waves / (double)(rounds * kSimds);
+}
+
+// Pure function of the shape: enough chunks that the launch has at least ~kTargetWaves
+// waves, preferring (among up to twice that many chunks) the smallest count whose waves
+// fill the SIMDs evenly; each chunk a multiple of the 32-key tile; partials are (d + 2)
+// floats per chunk, query row and head.  `total_len` is the most keys one sequence walks.
 DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int dtype) {
   DecodePlan p{1, total_len, 0, false};
   p.mfma = dtype == kBF16 && d % 16 == 0 && d <= 128 && total_len > 0;
@@ -458,6 +471,18 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
   const long long max_split = (total_len + kTile - 1) / kTile;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
+  if (units * want >= kSimds / 2) {
+    long long best = want;
+    double fill = simd_fill(units * want);
+    for (long long w = want + 1; w <= 2 * want && w <= max_split && fill < 0.9; ++w) {
+      const double f = simd_fill(units * w);
+      if (f > fill + 0.05) {
+        best = w;
+        fill = f;
+      }
+    }
+    want = best;
+  }
   long long chunk = (total_len + want - 1) / want;
   chunk = (chunk + kTile - 1) / kTile * kTile;
   p.chunk = (int)chunk;
