@@ -18,7 +18,8 @@
 // Angles are formed in double precision (the position times the pair's inverse
 // frequency, computed on the host in double, reduced modulo 2*pi), so their error does
 // not grow with the position; the reduced angle's sine and cosine and the rotation
-// itself are fp32.
+// itself are fp32.  A thread issues its row loads before the angle arithmetic, so the
+// two overlap.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -34,6 +35,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kHeadsPerThread = 2;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 // cos and sin of the angle of pair j at position p
 __device__ __forceinline__ void pair_sincos(long long p, int j, const double* inv_freq,
@@ -41,7 +43,10 @@ __device__ __forceinline__ void pair_sincos(long long p, int j, const double* in
   double inv = inv_freq[j];
   if (ff) inv /= (double)ff[j];
   const double ang = (double)p * inv;
-  const double r = ang - rint(ang / kTwoPi) * kTwoPi;  // |r| <= pi
+  // subtract the nearest whole number of turns; the rounded 1/(2 pi) can misplace the
+  // quotient only within ~1e-11 of a half turn, where rint's other choice leaves
+  // |r| <= pi + 1e-10 -- still an exact argument for sincosf
+  const double r = ang - rint(ang * kInvTwoPi) * kTwoPi;
   sincosf((float)r, &sn, &cs);
 }
 
@@ -90,19 +95,30 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
     row0 = ((long long)b * a.Hkv * a.L + p) * a.d;
   }
 
+  // the rows' loads go out first, so their latency overlaps the angle arithmetic
+  const long long src0 = tok * a.Hkv * a.d;  // [B, n, Hkv, d]: token tok, head 0
+  f32x4 k1s[kHeadsPerThread], k2s[kHeadsPerThread], v1s[kHeadsPerThread], v2s[kHeadsPerThread];
+#pragma unroll
+  for (int hh = 0; hh < kHeadsPerThread; ++hh) {
+    const int h = min(h0 + hh, h1 - 1);  // a missing last head re-reads one in bounds
+    const long long src = src0 + (long long)h * a.d;
+    k1s[hh] = *reinterpret_cast<const f32x4*>(a.k_new + src + j0);
+    k2s[hh] = *reinterpret_cast<const f32x4*>(a.k_new + src + half + j0);
+    v1s[hh] = *reinterpret_cast<const f32x4*>(a.v_new + src + j0);
+    v2s[hh] = *reinterpret_cast<const f32x4*>(a.v_new + src + half + j0);
+  }
+
   float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.rope) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) pair_sincos(p, j0 + e, a.inv_freq, a.freq_factors, cs[e], sn[e]);
   }
 
-  const long long src0 = tok * a.Hkv * a.d;  // [B, n, Hkv, d]: token tok, head 0
-  for (int h = h0; h < h1; ++h) {
-    const long long src = src0 + (long long)h * a.d;
-    const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.k_new + src + j0);
-    const f32x4 k2 = *reinterpret_cast<const f32x4*>(a.k_new + src + half + j0);
-    const f32x4 v1 = *reinterpret_cast<const f32x4*>(a.v_new + src + j0);
-    const f32x4 v2 = *reinterpret_cast<const f32x4*>(a.v_new + src + half + j0);
+#pragma unroll
+  for (int hh = 0; hh < kHeadsPerThread; ++hh) {
+    const int h = h0 + hh;
+    if (h >= h1) break;
+    const f32x4 k1 = k1s[hh], k2 = k2s[hh], v1 = v1s[hh], v2 = v2s[hh];
     f32x4 r1, r2;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
