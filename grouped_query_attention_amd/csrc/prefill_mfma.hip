@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace gqa {
@@ -322,7 +324,8 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   // pipeline over its blocks.  Region b runs the softmax of block b on the vector ALU
   // beside the S^T of block b+1 and the P V of block b-1 on the matrix core, so the
   // wave's own instruction stream keeps both busy.
-  auto interior_stage = [&](const char* kl, const char* vl) {
+  auto interior_stage = [&](const char* kl, const char* vl, int k0s, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     f32x16 s[kNB];
     bf16x8 pb[kNB][2];
     {
@@ -338,6 +341,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       if (b + 1 < kNB) read_k(kl + (b + 1) * kBlk * G_::kKStride, kf);
       if (b >= 1) read_v(vl + (b - 1) * kBlk * G_::kVStride, vf);
       float alpha;
+      if constexpr (kMasked) mask_blk(s[b], k0s + b * kBlk);
       const bool resc = softmax_blk(s[b], pb[b], alpha);
       if (b + 1 < kNB) mfma_s(kf, s[b + 1]);
       if (b >= 1) mfma_pv(vf, pb[b - 1]);
@@ -399,8 +403,16 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     bool inter = ks + kStage <= T;
     if (causal) inter = inter && ks + kStage - 1 <= qw;               // below the diagonal
     if (WIN && window > 0) inter = inter && ks > qw + 31 - window;    // inside every window
+    // A causal diagonal stage every block of which holds a key this wave's rows see runs
+    // the pipeline too, with the mask applied to each block's scores: a block no row of
+    // a column sees gives exact zeros (the column's running max is already finite), and
+    // the pipeline costs less than skipping the few invisible blocks saves.  (With a
+    // window the masked pipeline measured slower; those stages keep the edge path.)
+    const bool all_active = !WIN && causal && ks + kStage <= T && ks + kStage - kBlk <= qw + 31;
     if (inter)
-      interior_stage(cur, cur + G_::kKTile);
+      interior_stage(cur, cur + G_::kKTile, ks, std::false_type{});
+    else if (all_active)
+      interior_stage(cur, cur + G_::kKTile, ks, std::true_type{});
     else
       edge_stage(t, cur, cur + G_::kKTile);
     __builtin_amdgcn_s_waitcnt(0);  // stage t+1 has landed in LDS
