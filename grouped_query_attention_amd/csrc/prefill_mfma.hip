@@ -31,7 +31,7 @@
 //    four blocks: the softmax of block b (vector ALU) beside the S^T of block b+1 and
 //    the P V of block b-1 (matrix core), interleaved by sched_group_barrier.
 //  * Causal skipping: 32-key blocks entirely above a wave's diagonal are not computed;
-//    the mask is only evaluated on diagonal blocks.  A local window (the multi-query
+//    the mask is only evaluated in diagonal stages.  A local window (the multi-query
 //    primer's local attention, section 4.1: keys p-W+1 .. p) skips from both sides:
 //    stages below the workgroup's first window start are never loaded, blocks below a
 //    wave's window are not computed, and window-edge blocks are masked.
@@ -363,8 +363,8 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     pending = true;
   };
 
-  // Any other stage (diagonal, window edge, ragged end): block by block, with the
-  // visibility and mask checks.
+  // Any other stage (a diagonal with blocks the wave does not see, a window edge, a
+  // ragged end): block by block, with the visibility and mask checks.
   auto edge_stage = [&](int t, const char* kl, const char* vl) {
     if (pending) {
       mfma_pv(pend_v, pend_p);
