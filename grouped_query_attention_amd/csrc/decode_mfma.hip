@@ -471,11 +471,14 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
   const long long max_split = (total_len + kTile - 1) / kTile;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
-  if (units * want >= kSimds / 2) {
+  // chunks are whole tiles, so the split asked for and the split made can differ
+  auto chunk_for = [&](long long w) { return ((total_len + w - 1) / w + kTile - 1) / kTile * kTile; };
+  auto split_for = [&](long long w) { return (total_len + chunk_for(w) - 1) / chunk_for(w); };
+  if (units * split_for(want) >= kSimds / 2) {
     long long best = want;
-    double fill = simd_fill(units * want);
+    double fill = simd_fill(units * split_for(want));
     for (long long w = want + 1; w <= 2 * want && w <= max_split && fill < 0.9; ++w) {
-      const double f = simd_fill(units * w);
+      const double f = simd_fill(units * split_for(w));
       if (f > fill + 0.05) {
         best = w;
         fill = f;
@@ -483,8 +486,7 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
     }
     want = best;
   }
-  long long chunk = (total_len + want - 1) / want;
-  chunk = (chunk + kTile - 1) / kTile * kTile;
+  const long long chunk = chunk_for(want);
   p.chunk = (int)chunk;
   p.nsplit = (int)((total_len + chunk - 1) / chunk);
   p.workspace = (size_t)B * Hq * n * (size_t)p.nsplit * (size_t)(d + 2) * sizeof(float);

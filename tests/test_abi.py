@@ -132,6 +132,24 @@ def test_decode_plan_host_logic():
     assert gqa.attn_decode_workspace_bytes(1, 1, 8, 3, 2, 64, BF16) == 0
 
 
+def test_decode_plan_fills_the_simds():
+    """The split plan aims at two waves per SIMD (1024 SIMDs) and, where the history is
+    long enough to allow it, picks a chunk count whose waves fill the SIMDs to >= 90%
+    (a partial last round of equal waves leaves SIMDs idle).  Chunks are whole 32-key
+    tiles, so not every history admits such a count (1 x 100000 keys splits into 1563 or
+    3125 chunks, both 76%); the shapes below all do."""
+    simds = 1024
+    for (B, n, L, Hq, Hkv, d) in [(64, 1, 32768, 32, 8, 128), (64, 4, 32768, 32, 8, 128), (48, 1, 32768, 32, 8, 128),
+                                  (5, 1, 65536, 32, 8, 128), (1, 1, 98304, 8, 1, 64), (32, 2, 8192, 16, 4, 128)]:
+        splits = gqa.attn_decode_num_splits(B, n, L, Hq, Hkv, d, BF16)
+        units = B * Hkv * -(-((Hq // Hkv) * n) // 16)
+        waves = units * splits
+        assert waves >= simds, (B, n, L, splits)
+        assert waves / (-(-waves // simds) * simds) >= 0.9, (B, n, L, splits, waves)
+    # the contiguous 64-sequence, 32768-key cache: 8 KV heads x 64 sequences x 4 chunks = 2048 waves
+    assert gqa.attn_decode_num_splits(64, 1, 32768, 32, 8, 128, BF16) == 4
+
+
 A4 = 0x10004  # 4-byte aligned, not 16-byte aligned
 
 
