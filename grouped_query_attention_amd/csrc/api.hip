@@ -117,7 +117,7 @@ int decode_impl(const void* q, const void* kcache, const void* vcache, float* ou
   }
   const long long sd = d_h;
   gqa::GenericArgs a{q, kcache, vcache, out, dtype, B, Hq, Hkv, newTokens, totalLen, d_h, scale,
-                     1, startPos, (long long)newTokens * Hq * sd, sd, (long long)Hq * sd, window};
+                     1, startPos, (long long)newTokens * Hq * sd, sd, (long long)Hq * sd, window, nullptr};
   return status_of(gqa::launch_attn_generic(a, s));
 }
 

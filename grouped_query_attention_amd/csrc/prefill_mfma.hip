@@ -102,7 +102,6 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   // the local window is a separate instantiation: plain causal attention carries none
   // of its checks
   const int window = WIN ? window_arg : 0;
-  constexpr int NT = kWgWaves * 64;
   constexpr int SLICES = kWgWaves / HPW;  // 32-row slices per head
   constexpr int QT = 32 * SLICES;         // query rows per head per workgroup
   // Two stages in two separate LDS arrays: the loop is unrolled by two so each
