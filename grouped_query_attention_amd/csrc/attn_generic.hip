@@ -8,8 +8,8 @@
 // j >= pos0 + i - W + 1 (the multi-query primer's local attention, section 4.1).
 //
 // Work split: a 256-thread block owns 32 query rows of one query head; each row
-// is served by 8 lanes, each lane holding DPL of the head dims (dims c, c+8,
-// c+16, ... for lane c, so the 8 lanes of a row touch consecutive elements).
+// is served by 8 lanes, each lane holding DPL consecutive head dims (c*DPL ..
+// c*DPL + DPL - 1 for lane c), so its K and V reads from LDS are 16-byte vectors.
 // Key/value tiles of 32 keys are staged through LDS in float32 and shared by the
 // 32 rows.  Softmax is the online recurrence (running max m and normalizer l in
 // log2 units, numerator rescaled when m grows), which equals the materialized
@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
     float* __restrict__ out, int Hq, int Hkv, int Tq, int Tk, int d, float scale_log2, int causal,
     int pos0, int window, long long q_sb, long long q_sh, long long q_st, float* __restrict__ lse) {
   constexpr int DP = DPL * kLanesPerRow;  // padded head dim held by one row
-  __shared__ float Ks[kKeysPerTile * DP];
-  __shared__ float Vs[kKeysPerTile * DP];
+  __shared__ __attribute__((aligned(16))) float Ks[kKeysPerTile * DP];
+  __shared__ __attribute__((aligned(16))) float Vs[kKeysPerTile * DP];
 
   const int tid = threadIdx.x;
   const int r = tid / kLanesPerRow;  // row within the block
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
   float qr[DPL], o[DPL];
 #pragma unroll
   for (int u = 0; u < DPL; ++u) {
-    const int e = c + kLanesPerRow * u;
+    const int e = c * DPL + u;
     qr[u] = (row_ok && e < d) ? to_f32(q[qoff + e]) * scale_log2 : 0.f;
     o[u] = 0.f;
   }
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
     for (int jj = 0; jj < kKeysPerTile; ++jj) {
       float part = 0.f;
 #pragma unroll
-      for (int u = 0; u < DPL; ++u) part += qr[u] * Ks[jj * DP + c + kLanesPerRow * u];
+      for (int u = 0; u < DPL; ++u) part += qr[u] * Ks[jj * DP + c * DPL + u];
       // sum over the 8 lanes of the row; every lane ends with the same value
       part += __shfl_xor(part, 1);
       part += __shfl_xor(part, 2);
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
       const float p = __builtin_amdgcn_exp2f(s[jj] - m_ref);
       l += p;
 #pragma unroll
-      for (int u = 0; u < DPL; ++u) o[u] += p * Vs[jj * DP + c + kLanesPerRow * u];
+      for (int u = 0; u < DPL; ++u) o[u] += p * Vs[jj * DP + c * DPL + u];
     }
     m = m_new;
   }
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
     if (lse && c == 0) lse[((long long)b * Hq + h) * Tq + i] = (m + __log2f(l)) * 0.6931471805599453f;
 #pragma unroll
     for (int u = 0; u < DPL; ++u) {
-      const int e = c + kLanesPerRow * u;
+      const int e = c * DPL + u;
       if (e < d) out[qoff + e] = o[u] * inv;
     }
   }
