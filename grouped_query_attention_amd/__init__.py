@@ -26,7 +26,8 @@ GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
 EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_prefill_window", "attn_decode_workspace_bytes",
             "attn_decode_num_splits", "attn_decode_cached", "attn_decode_window_workspace_bytes",
             "attn_decode_window", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
-            "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_kv_append",
+            "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_decode_blocks",
+            "attn_kv_append",
             "attn_kv_append_paged", "attn_prefill_lse", "attn_backward_workspace_bytes", "attn_backward",
             "attn_strerror")
 
@@ -62,6 +63,9 @@ lib.attn_decode_paged_window_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i,
 lib.attn_decode_paged_window.restype = _i
 lib.attn_decode_paged_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                          _i, _i, _vp, _sz, _vp]
+lib.attn_decode_blocks.restype = _i
+lib.attn_decode_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                   _vp, _sz, _vp]
 lib.attn_kv_append.restype = _i
 lib.attn_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]
 lib.attn_kv_append_paged.restype = _i
@@ -257,6 +261,43 @@ def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspac
         what = "attn_decode_paged_window"
     if rc != GQA_OK:
         raise GQAError(rc, what)
+    return out
+
+
+def attn_decode_blocks(q, kpool, vpool, block_table, seq_lens, out=None, workspace=None, stream=None):
+    """Cached decode over token-major blocks (makarna's CausalAttentionBlocks views).
+    q [B,n,Hq,d] bf16; kpool, vpool [num_blocks,block_size,Hkv,d] bf16; block_table
+    [B,max_blocks] and seq_lens [B] int32 on the GPU, as in attn_decode_paged.  Scale is
+    1/sqrt(d).  Returns out [B,n,Hq,d] float32."""
+    B, n, Hq, d = q.shape
+    if kpool.dim() != 4 or kpool.shape[3] != d or vpool.shape != kpool.shape:
+        raise ValueError("kpool, vpool must be [num_blocks, block_size, Hkv, d]; got %s %s"
+                         % (tuple(kpool.shape), tuple(vpool.shape)))
+    if kpool.dtype != q.dtype or vpool.dtype != q.dtype:
+        raise TypeError("q, kpool, vpool must share one dtype")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]; got %s %s"
+                         % (tuple(block_table.shape), tuple(seq_lens.shape)))
+    num_blocks, bs, Hkv = kpool.shape[0], kpool.shape[1], kpool.shape[2]
+    max_blocks = block_table.shape[1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32:
+        raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
+    need = attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.attn_decode_blocks(_dev_ptr(q, "q"), _dev_ptr(kpool, "kpool"), _dev_ptr(vpool, "vpool"),
+                                _dev_ptr(block_table, "block_table"), _dev_ptr(seq_lens, "seq_lens"),
+                                _dev_ptr(out, "out"), B, n, Hq, Hkv, d, bs, max_blocks, num_blocks, dt,
+                                ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_decode_blocks")
     return out
 
 

@@ -136,7 +136,7 @@ int paged_impl(const void* q, const void* kpool, const void* vpool,
                       const int* block_table, const int* seq_lens, float* out, int B,
                       int newTokens, int Hq, int Hkv, int d_h, int block_size, int max_blocks,
                       int num_blocks, int window, int dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, bool token_major = false) {
   int rc = paged_check(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, num_blocks, dtype);
   if (rc != GQA_OK) return rc;
   if (window < 0) return GQA_EINVAL;
@@ -153,7 +153,7 @@ int paged_impl(const void* q, const void* kpool, const void* vpool,
   if (plan.workspace > 0 && !aligned16(workspace)) return GQA_EINVAL;
   gqa::DecodeArgs a{q, kpool, vpool, out, B, newTokens, Hq, Hkv, max_len, d_h, 0,
                     1.0f / sqrtf((float)d_h), workspace, window};
-  gqa::PagedArgs pg{block_table, seq_lens, block_size, max_blocks, num_blocks};
+  gqa::PagedArgs pg{block_table, seq_lens, block_size, max_blocks, num_blocks, token_major};
   return status_of(gqa::launch_attn_decode_paged(a, pg, plan, static_cast<hipStream_t>(stream)));
 }
 
@@ -265,6 +265,15 @@ int attn_decode_paged(const void* q, const void* kpool, const void* vpool, const
   return paged_impl(q, kpool, vpool, block_table, seq_lens, out, B, newTokens, Hq, Hkv, d_h,
                     block_size, max_blocks, num_blocks, 0, dtype, workspace, workspace_bytes,
                     stream);
+}
+
+int attn_decode_blocks(const void* q, const void* kpool, const void* vpool, const int* block_table,
+                       const int* seq_lens, float* out, int B, int newTokens, int Hq, int Hkv,
+                       int d_h, int block_size, int max_blocks, int num_blocks, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return paged_impl(q, kpool, vpool, block_table, seq_lens, out, B, newTokens, Hq, Hkv, d_h,
+                    block_size, max_blocks, num_blocks, 0, dtype, workspace, workspace_bytes,
+                    stream, true);
 }
 
 int attn_decode_paged_window(const void* q, const void* kpool, const void* vpool,

@@ -62,8 +62,10 @@ struct DGeo {
   static constexpr int kLdsPerWave = kTile * kVStride;
 };
 
-// Where the K/V history lives: one contiguous [B, Hkv, L, d] cache, or a pool of
-// blocks [num_blocks, Hkv, bs, d] addressed through a per-sequence block table.
+// Where the K/V history lives: one contiguous [B, Hkv, L, d] cache, or a pool of blocks
+// addressed through a per-sequence block table.  A block is head-major [Hkv, bs, d]
+// (rstride d, hstride bs*d) or token-major [bs, Hkv, d] (rstride Hkv*d, hstride d); its
+// rows are 2*d contiguous bytes either way.
 struct KvSource {
   const uint16_t* k;
   const uint16_t* v;
@@ -73,6 +75,8 @@ struct KvSource {
   int start_pos;     // contiguous: position of the first new token (every sequence)
   int bs, max_blocks, num_blocks, max_len;  // paged
   int window;        // local window (keys p-W+1 .. p); 0 = none
+  int rstride;                 // paged: elements from one position to the next of a head
+  long long hstride, bstride;  // paged: elements from one K/V head to the next; per block
 };
 
 // First key the kernels walk: the first new token's window start, rounded down to the
@@ -152,11 +156,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
   }
 
   // Where a 32-key tile's rows live.  A tile is two 16-row groups; group kb covers rows
-  // j0+16kb .. j0+16kb+15, clamped to `last`.  Rows of one group are consecutive in
-  // memory: in the contiguous cache trivially, in a pool because a block holds a
-  // multiple of 16 positions.  rows[kb] is the element offset of the group's first
-  // (clamped) row; row r of the group is at rows[kb] + (min(j0+16kb+r, last) - first)*D.
+  // j0+16kb .. j0+16kb+15, clamped to `last`.  Rows of one group are evenly spaced in
+  // memory (rs elements apart): in the contiguous cache trivially, in a pool because a
+  // block holds a multiple of 16 positions.  rows[kb] is the element offset of the
+  // group's first (clamped) row; row r of the group is at
+  // rows[kb] + (min(j0+16kb+r, last) - first)*rs.
   const long long head_base = ((long long)b * Hkv + g) * (long long)kv.L * D;  // contiguous
+  const int rs = PAGED ? kv.rstride : D;
   const int* tab = PAGED ? kv.table + (long long)b * kv.max_blocks : nullptr;
   bool bad = false;  // a table entry outside the pool: the sequence's rows become NaN
   // table entries of a tile's two groups; fetched one tile ahead of the K/V loads with
@@ -181,7 +187,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
           bad = true;
           ent = 0;
         }
-        rows[kb] = (((long long)ent * Hkv + g) * kv.bs + first % kv.bs) * D;
+        rows[kb] = (long long)ent * kv.bstride + (long long)g * kv.hstride +
+                   (long long)(first % kv.bs) * kv.rstride;
       } else {
         rows[kb] = head_base + (long long)first * D;
       }
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int first = min(j0 + 16 * kb, last);
-      const long long row = rows[kb] + (long long)(min(j0 + 16 * kb + col, last) - first) * D;
+      const long long row = rows[kb] + (long long)(min(j0 + 16 * kb + col, last) - first) * rs;
 #pragma unroll
       for (int st = 0; st < G_::kSteps; ++st) {
         const int d0 = 32 * st + 8 * grp;
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
       const int r = ch / (D / 8), cc = ch % (D / 8);
       const int kb = r >> 4;
       const int first = min(j0 + 16 * kb, last);
-      const long long row = (kb ? rows[1] : rows[0]) + (long long)(min(j0 + r, last) - first) * D;
+      const long long row = (kb ? rows[1] : rows[0]) + (long long)(min(j0 + r, last) - first) * rs;
       vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kv.v + row + cc * 8));
     }
   };
@@ -495,7 +502,7 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
 
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), nullptr,
-              nullptr, a.L, a.start_pos, 0, 0, 0, 0, a.window};
+              nullptr, a.L, a.start_pos, 0, 0, 0, 0, a.window, a.d, 0, 0};
   return launch_any_d<false>(a, kv, p, stream);
 }
 
@@ -503,7 +510,16 @@ hipError_t launch_attn_decode_paged(const DecodeArgs& a, const PagedArgs& pg, co
                                     hipStream_t stream) {
   KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), pg.table,
               pg.seq_lens, 0, 0, pg.block_size, pg.max_blocks, pg.num_blocks,
-              pg.block_size * pg.max_blocks, a.window};
+              pg.block_size * pg.max_blocks, a.window, 0, 0, 0};
+  const long long d = a.d, bs = pg.block_size, blk = (long long)a.Hkv * bs * d;
+  if (pg.token_major) {  // [num_blocks, bs, Hkv, d]
+    kv.rstride = a.Hkv * a.d;
+    kv.hstride = d;
+  } else {  // [num_blocks, Hkv, bs, d]
+    kv.rstride = a.d;
+    kv.hstride = bs * d;
+  }
+  kv.bstride = blk;
   return launch_any_d<true>(a, kv, p, stream);
 }
 

@@ -72,12 +72,14 @@ struct DecodeArgs {
 };
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
 
-// Paged history: kc/vc of DecodeArgs are the block pools [num_blocks, Hkv, block_size, d];
-// L and start_pos of DecodeArgs are unused (each sequence has its own length).
+// Paged history: kc/vc of DecodeArgs are the block pools, [num_blocks, Hkv, block_size, d]
+// (head-major blocks) or [num_blocks, block_size, Hkv, d] (token_major); L and start_pos
+// of DecodeArgs are unused (each sequence has its own length).
 struct PagedArgs {
   const int* table;     // [B, max_blocks], device
   const int* seq_lens;  // [B], device
   int block_size, max_blocks, num_blocks;
+  bool token_major;
 };
 hipError_t launch_attn_decode_paged(const DecodeArgs& a, const PagedArgs& pg, const DecodePlan& p,
                                     hipStream_t stream);

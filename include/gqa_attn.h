@@ -187,6 +187,28 @@ int attn_decode_paged(const void* q, const void* kpool, const void* vpool,
                       void* stream);
 
 /*
+ * Cached decode over token-major KV blocks: makarna's CausalAttentionBlocks, whose views
+ * each hold Length consecutive positions from Start on, K and V laid out token by token
+ * with all KV heads of a token together ([t, Hkv*headDim]).  Here the views are the
+ * blocks a block table names: logical block i of sequence b is the view with Start =
+ * i*block_size and Length = min(block_size, seq_lens[b] - Start), so its key positions
+ * are fixed by its place in the table.  Per sequence the result is exactly
+ * attn_decode_paged (and attn_decode_cached) over the same history.
+ *
+ *   kpool, vpool    : [num_blocks, block_size, Hkv, d_h]  physical blocks, token-major
+ *                     inside each block: [tokenWithinBlock][kvHead][headDim]
+ *   everything else : as attn_decode_paged, workspace included
+ *                     (attn_decode_paged_workspace_bytes(...) bytes)
+ *
+ * Supported shapes and every error case are those of attn_decode_paged.
+ */
+int attn_decode_blocks(const void* q, const void* kpool, const void* vpool,
+                       const int* block_table, const int* seq_lens, float* out, int B,
+                       int newTokens, int Hq, int Hkv, int d_h, int block_size, int max_blocks,
+                       int num_blocks, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Local-window paged decode: attn_decode_paged where new token i of sequence b
  * (position seq_lens[b] - newTokens + i) sees only the last `window` positions up to
  * its own.  Table entries of blocks that lie entirely below the first new token's

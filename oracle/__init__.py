@@ -18,7 +18,11 @@ cached decode, makarna's ``CausalAttentionCached``: the new tokens sit at
 absolute positions startPos .. startPos+newTokens-1, each sees every cached key
 up to and including its own position, and the scale is 1/sqrt(headDim).
 Paged decode (makarna's ``CausalAttentionPackedBlocks``) is that same cached
-decode over the history assembled from the blocks a block table names.
+decode over the history assembled from the blocks a block table names.  The
+views form (makarna's ``CausalAttentionBlocks``) is written out on its own terms
+in ``decode_views``: a list of token-major views, each holding the keys at
+positions Start .. Start+Length-1, of which new token i sees those below
+startPos+i+1.
 
 Inputs are widened exactly to float64 (bf16 and fp32 values are all exactly
 representable), so the oracle never rounds an input.
@@ -178,6 +182,92 @@ def decode_paged(q, kpool, vpool, block_table, seq_lens, block_size: int, nthrea
         kh = gather_paged(kpool, block_table, L, block_size, b)
         vh = gather_paged(vpool, block_table, L, block_size, b)
         out[b] = decode_cached(q[b:b + 1], kh[None], vh[None], L - n, nthreads, window)[0]
+    return out
+
+
+def decode_views(q, views, start_pos: int, n_kv_heads: int):
+    """makarna's CausalAttentionBlocks for one sequence, materialized in float64.
+
+    q: [n, Hq, d] new-token queries (token-major).  views: iterable of (start, K, V),
+    K and V [length, Hkv*d] token-major (all KV heads of a position side by side),
+    holding the keys at absolute positions start .. start+length-1.  New token i sits
+    at start_pos+i and sees every key of every view whose position is below
+    start_pos+i+1; the views are taken in order of start (their order in the list
+    does not matter) and a view of length 0 holds nothing.  Query head h reads KV
+    head h // (Hq // Hkv); the scale is 1/sqrt(d).  A token that sees no key gets a
+    zero row, as the page's loop leaves it.  Returns [n, Hq, d] (float64).
+    """
+    q = to_f64(q)
+    n, Hq, d = q.shape
+    if Hq % n_kv_heads:
+        raise ValueError("Hq %d is not a multiple of Hkv %d" % (Hq, n_kv_heads))
+    group = Hq // n_kv_heads
+    vs = []
+    for start, kv_k, kv_v in views:
+        kv_k, kv_v = to_f64(kv_k), to_f64(kv_v)
+        if kv_k.shape != kv_v.shape or kv_k.ndim != 2 or kv_k.shape[1] != n_kv_heads * d:
+            raise ValueError("a view's K and V must both be [length, Hkv*d]")
+        if kv_k.shape[0] > 0:
+            vs.append((int(start), kv_k.reshape(-1, n_kv_heads, d), kv_v.reshape(-1, n_kv_heads, d)))
+    vs.sort(key=lambda t: t[0])
+    scale = 1.0 / math.sqrt(d)
+    out = np.zeros((n, Hq, d), dtype=np.float64)
+    for i in range(n):
+        limit = start_pos + i + 1  # keys at positions < limit are visible
+        ks, vv = [], []
+        for start, vk, vval in vs:
+            if start >= limit:
+                continue
+            m = min(vk.shape[0], limit - start)
+            ks.append(vk[:m])
+            vv.append(vval[:m])
+        if not ks:
+            continue
+        kc, vc = np.concatenate(ks), np.concatenate(vv)  # [keys, Hkv, d]
+        for h in range(Hq):
+            s_ = (kc[:, h // group, :] @ q[i, h]) * scale
+            w = np.exp(s_ - s_.max())
+            out[i, h] = (w / w.sum()) @ vc[:, h // group, :]
+    return out
+
+
+def views_from_blocks(kpool, vpool, block_table, seq_len: int, block_size: int, b: int):
+    """The views of sequence b out of token-major block pools [num_blocks, block_size,
+    Hkv, d]: logical block i is the view with Start = i*block_size and Length =
+    min(block_size, seq_len - Start), its K and V the first Length rows of physical
+    block block_table[b][i], each row [Hkv*d]."""
+    kpool, vpool = to_f64(kpool), to_f64(vpool)
+    nb, bs, hkv, d = kpool.shape
+    if bs != block_size or vpool.shape != kpool.shape:
+        raise ValueError("pools must be [num_blocks, %d, Hkv, d]" % block_size)
+    table = np.asarray(block_table)
+    views = []
+    for i in range(-(-seq_len // block_size)):
+        blk = int(table[b, i])
+        if blk < 0 or blk >= nb:
+            raise ValueError("sequence %d: block id out of range" % b)
+        length = min(block_size, seq_len - i * block_size)
+        views.append((i * block_size, kpool[blk, :length].reshape(length, hkv * d),
+                      vpool[blk, :length].reshape(length, hkv * d)))
+    return views
+
+
+def decode_blocks(q, kpool, vpool, block_table, seq_lens, block_size: int):
+    """Cached decode over token-major blocks: decode_views of every sequence b over the
+    views of its table row, with its new tokens at seq_lens[b]-n .. seq_lens[b]-1.
+    q [B,n,Hq,d] -> out [B,n,Hq,d] (float64)."""
+    q = to_f64(q)
+    B, n, Hq, d = q.shape
+    hkv = int(kpool.shape[2])
+    out = np.zeros((B, n, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < n:
+            raise ValueError("sequence %d: length %d < newTokens %d" % (b, L, n))
+        if n == 0:
+            continue
+        views = views_from_blocks(kpool, vpool, block_table, L, block_size, b)
+        out[b] = decode_views(q[b], views, L - n, hkv)
     return out
 
 

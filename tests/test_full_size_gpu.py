@@ -105,4 +105,13 @@ def test_full_size_paged_decode(gqa, decode_data, cfg):
     err = float(np.abs(p[b:b + 1, :, heads].cpu().double().numpy() - want).max())
     print("%s paged sampled max-abs error %.3g" % (cfg.name, err))
     assert err <= TOL[cfg.dtype], err
-    del kp, vp
+    # the same blocks token-major (attn_decode_blocks): again exactly the contiguous result
+    kt = kp.permute(0, 2, 1, 3).contiguous()
+    del kp
+    vt = vp.permute(0, 2, 1, 3).contiguous()
+    del vp
+    print("%s token-major blocks" % cfg.name, flush=True)
+    t = gqa.attn_decode_blocks(q.cuda(), kt, vt, table, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a, t)
+    del kt, vt
