@@ -77,6 +77,7 @@ struct KvSource {
   int window;        // local window (keys p-W+1 .. p); 0 = none
   int rstride;                 // paged: elements from one position to the next of a head
   long long hstride, bstride;  // paged: elements from one K/V head to the next; per block
+  int head_fast;  // 1: consecutive waves take the K/V heads of one (sequence, chunk)
 };
 
 // First key the kernels walk: the first new token's window start, rounded down to the
@@ -113,12 +114,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(
   const int wave = threadIdx.x >> 6;
   const int gw = blockIdx.x * kWaves + wave;
   if (gw >= total_waves) return;  // whole wave; no workgroup barrier is used
-  const int split = gw % nsplit;
-  const int unit = gw / nsplit;
-  const int cb = unit % ncb;
-  const int bg = unit / ncb;
-  const int g = bg % Hkv;
-  const int b = bg / Hkv;
+  // wave -> (sequence b, K/V head g, column block cb, chunk split).  With token-major
+  // blocks the K/V heads of a position share its rows, so their waves go side by side.
+  int split, cb, g, b;
+  if (kv.head_fast) {
+    g = gw % Hkv;
+    const int r = gw / Hkv;
+    split = r % nsplit;
+    cb = (r / nsplit) % ncb;
+    b = r / nsplit / ncb;
+  } else {
+    split = gw % nsplit;
+    const int unit = gw / nsplit;
+    cb = unit % ncb;
+    g = unit / ncb % Hkv;
+    b = unit / ncb / Hkv;
+  }
   const int G = Hq / Hkv;
   const int ncols = G * n;
   int kv_len;  // keys any new token can see: the sequence's history length
@@ -502,7 +513,7 @@ DecodePlan plan_decode(int B, int n, int total_len, int Hq, int Hkv, int d, int 
 
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), nullptr,
-              nullptr, a.L, a.start_pos, 0, 0, 0, 0, a.window, a.d, 0, 0};
+              nullptr, a.L, a.start_pos, 0, 0, 0, 0, a.window, a.d, 0, 0, 0};
   return launch_any_d<false>(a, kv, p, stream);
 }
 
@@ -510,11 +521,12 @@ hipError_t launch_attn_decode_paged(const DecodeArgs& a, const PagedArgs& pg, co
                                     hipStream_t stream) {
   KvSource kv{static_cast<const uint16_t*>(a.kc), static_cast<const uint16_t*>(a.vc), pg.table,
               pg.seq_lens, 0, 0, pg.block_size, pg.max_blocks, pg.num_blocks,
-              pg.block_size * pg.max_blocks, a.window, 0, 0, 0};
+              pg.block_size * pg.max_blocks, a.window, 0, 0, 0, 0};
   const long long d = a.d, bs = pg.block_size, blk = (long long)a.Hkv * bs * d;
   if (pg.token_major) {  // [num_blocks, bs, Hkv, d]
     kv.rstride = a.Hkv * a.d;
     kv.hstride = d;
+    kv.head_fast = 1;
   } else {  // [num_blocks, Hkv, bs, d]
     kv.rstride = a.d;
     kv.hstride = bs * d;
