@@ -20,7 +20,7 @@ LIB_NAME = "libgqa_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.hip", "attn_generic.hip", "prefill_mfma.hip", "decode_mfma.hip", "kv_append.hip",
-           "backward_mfma.hip", "backward_generic.hip"]
+           "backward_mfma.hip", "backward_generic.hip", "prefill_f32_mfma.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.
@@ -31,6 +31,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The fp32 matrix-core prefill keeps its MFMA operands and
+# accumulators in ordinary VGPRs: in the default form the compiler copied every
+# accumulator through AGPRs around the softmax rescale (about ten copies per product).
+EXTRA_FLAGS = {"prefill_f32_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")
@@ -39,7 +45,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -38,7 +38,9 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
   if (T > kMaxSeq) return GQA_EUNSUPPORTED;
   // an explicit kernel request is checked even for empty tensors, so a zero-size call
   // tells the caller whether that kernel covers the shape
-  const bool mfma_ok = gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
+  const bool mfma_ok = dtype == GQA_F32
+                           ? window == 0 && gqa::prefill_f32_mfma_supported(d_h, Hq, Hkv)
+                           : gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
   if (algo == GQA_ALGO_MFMA && !mfma_ok) return GQA_EUNSUPPORTED;
   if (B == 0 || T == 0) return GQA_OK;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_EINVAL;
@@ -46,6 +48,7 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (algo == GQA_ALGO_MFMA || (algo == GQA_ALGO_AUTO && mfma_ok)) {
     gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window, lse};
+    if (dtype == GQA_F32) return status_of(gqa::launch_attn_prefill_f32_mfma(a, s));
     return status_of(gqa::launch_attn_prefill_mfma(a, s));
   }
   const long long sd = d_h;

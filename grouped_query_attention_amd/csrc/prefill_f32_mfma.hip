@@ -1,0 +1,235 @@
+// prefill_f32_mfma.hip -- fp32 causal GQA prefill on the fp32 matrix cores.
+//
+// Same computation as the other prefill kernels (scores = scale * Q K^T, causal mask,
+// softmax over keys, times V; query head h reads K/V head h / (Hq/Hkv)), with fp32
+// inputs kept in fp32: the products run on v_mfma_f32_32x32x2_f32, which multiplies
+// and accumulates in fp32.  The online softmax (running max and normalizer, numerator
+// rescaled when the max grows) is the exact recurrence of Riftco's "Two exact
+// full-sequence algorithms"; it equals the materialized softmax up to rounding.
+//
+// Work split: a 256-thread workgroup owns 128 query rows of one query head, one wave
+// per 32 rows.  Key tiles of 32 keys are staged through LDS: K row-major, V transposed,
+// each loaded from HBM into registers one tile ahead.
+//
+// Per wave and tile:
+//   S^T = K Q^T   A = K (32 keys x 2 head dims per step, from LDS), B = Q^T (registers).
+//                 Lane l owns query l%32 and, in its 16 accumulator registers, keys
+//                 8*(r/4) + 4*(l/32) + r%4: the row max is an in-lane max plus one swap
+//                 with lane l^32.  Lane half h = l/32 holds head dims h*D/2 .. of both
+//                 operands, so each step sums two head dims D/2 apart.
+//   O^T += V^T P^T  A = V^T (32 head dims x 2 keys, from the transposed LDS tile),
+//                 B = P^T straight from the score registers: step t takes key
+//                 8*(t/4) + 4*(l/32) + t%4, which is exactly register t of the lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace gqa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kRows = 32;                    // query rows per wave
+constexpr int kKeys = 32;                    // keys per tile
+constexpr int kThreads = kWaves * 64;
+constexpr int kVtStride = kKeys + 4;         // floats per V^T row: 9 16-byte chunks (odd)
+
+template <int D>
+struct F32Geo {
+  static constexpr int KStride = D + 4;      // floats per K row: an odd number of 16-byte chunks
+  static constexpr int Half = D / 2;         // head dims per lane half
+  static constexpr int DB = D / 32;          // 32-dim blocks of O^T
+  static constexpr int C4 = D / 4;           // 16-byte chunks per row
+  static constexpr int LPT = kKeys * C4 / kThreads;  // chunks per thread per tensor and tile
+  static_assert(D % 32 == 0 && LPT * kThreads == kKeys * C4, "D must be a multiple of 32");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int T, float scale_log2,
+    int causal) {
+  using G = F32Geo<D>;
+  __shared__ __attribute__((aligned(16))) float Ks[kKeys * G::KStride];
+  __shared__ __attribute__((aligned(16))) float Vt[D * kVtStride];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest q-tiles first
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = hq / (Hq / Hkv);
+  const int q0 = qt * (kWaves * kRows) + wave * kRows;  // the wave's first query row
+  const int qi = q0 + col;                              // the lane's query row
+  const long long qbase = ((long long)b * Hq + hq) * (long long)T * D;
+  const long long kvbase = ((long long)b * Hkv + g) * (long long)T * D;
+
+  // Q^T fragment: head dims h*D/2 .. h*D/2 + D/2 - 1 of the lane's row, times scale*log2(e)
+  // so that scores come out in log2 units.  Rows past T are zero (never stored).
+  float qf[G::Half];
+  {
+    const bool ok = qi < T;
+    const float* src = q + qbase + (long long)(ok ? qi : 0) * D + h * G::Half;
+#pragma unroll
+    for (int u = 0; u < G::Half / 4; ++u) {
+      f32x4 x = ok ? *reinterpret_cast<const f32x4*>(src + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * u + e] = x[e] * scale_log2;
+    }
+  }
+
+  // keys the workgroup walks, and the keys this wave sees (none for a wave past T)
+  const int wg_rows_end = min(T, (qt + 1) * kWaves * kRows);
+  const int kend = causal ? wg_rows_end : T;
+  const int wave_kend = q0 >= T ? 0 : (causal ? min(T, q0 + kRows) : T);
+
+  // tile staging: chunk c = threadIdx.x + kThreads*i is key c / C4, head dims 4*(c % C4) ..
+  f32x4 kr[G::LPT], vr[G::LPT];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < G::LPT; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int j = j0 + c / G::C4;
+      const long long off = kvbase + (long long)j * D + 4 * (c % G::C4);
+      if (j < T) {
+        kr[i] = *reinterpret_cast<const f32x4*>(k + off);
+        vr[i] = *reinterpret_cast<const f32x4*>(v + off);
+      } else {
+        kr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < G::LPT; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int key = c / G::C4, e0 = 4 * (c % G::C4);
+      *reinterpret_cast<f32x4*>(Ks + key * G::KStride + e0) = kr[i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Vt[(e0 + u) * kVtStride + key] = vr[i][u];
+    }
+  };
+
+  f32x16 o[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = -INFINITY;  // running max of the lane's query (log2 units), shared by both halves
+  float l = 0.f;        // this lane's share of the normalizer (its 16 keys of every tile)
+
+  if (kend > 0) load(0);
+  for (int j0 = 0; j0 < kend; j0 += kKeys) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store();
+    __syncthreads();
+    if (j0 + kKeys < kend) load(j0 + kKeys);  // in flight during this tile's products
+    if (j0 >= wave_kend) continue;            // wave-uniform: no key here is visible
+
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const float* krow = Ks + col * G::KStride + h * G::Half;
+#pragma unroll
+    for (int u = 0; u < G::Half / 4; ++u) {
+      const f32x4 kk = *reinterpret_cast<const f32x4*>(krow + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[e], qf[4 * u + e], s, 0, 0, 0);
+    }
+
+    // mask keys past T and, on the diagonal, keys after the query
+    if (j0 + kKeys > T || (causal && j0 + kKeys - 1 > q0)) {  // wave-uniform
+      const int lim = causal ? min(T - 1, qi) : T - 1;  // last key the lane's query sees
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        s[r] = key <= lim ? s[r] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;  // no visible key yet
+    const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
+      l += p[r];
+    }
+
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+      const float* vrow = Vt + (32 * db + col) * kVtStride + 4 * h;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const f32x4 vv = *reinterpret_cast<const f32x4*>(vrow + 8 * t4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[u], p[4 * t4 + u], o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (q0 < T) {  // wave-uniform
+    const float lt = l + __shfl_xor(l, 32);
+    if (qi < T) {
+      const float inv = 1.f / lt;
+      float* dst = out + qbase + (long long)qi * D;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          f32x4 x;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = o[db][4 * rr + u] * inv;
+          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * rr + 4 * h) = x;
+        }
+      // row log-sum-exp of the scaled scores, natural log
+      if (lse && h == 0)
+        lse[((long long)b * Hq + hq) * T + qi] = (m + __log2f(lt)) * 0.6931471805599453f;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
+  dim3 grid((a.T + kWaves * kRows - 1) / (kWaves * kRows), a.Hq, a.B);
+  hipLaunchKernelGGL((prefill_f32_kernel<D>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), a.out, a.lse, a.Hq, a.Hkv, a.T,
+                     a.scale * 1.4426950408889634f, a.causal);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_f32_mfma_supported(int d, int Hq, int Hkv) {
+  return d > 0 && d <= 128 && d % 32 == 0 && Hkv > 0 && Hq % Hkv == 0;
+}
+
+hipError_t launch_attn_prefill_f32_mfma(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 32: return launch_f32<32>(a, stream);
+    case 64: return launch_f32<64>(a, stream);
+    case 96: return launch_f32<96>(a, stream);
+    case 128: return launch_f32<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gqa

@@ -158,8 +158,12 @@ def test_rows_sum_to_one(gqa, dtype, d):
     v = torch.ones_like(k)
     for algo in algos_for(dtype, d):
         got = run_prefill(gqa, q, k, v, 1 / math.sqrt(d), True, ALGOS[algo])
-        tol = 1e-6 if dtype == "f32" else 1e-2
-        assert float((got - 1).abs().max()) <= tol
+        # out = (sum_j p_j * 1) / (sum_j p_j); a kernel may form the two sums in different
+        # orders (the fp32 matrix-core kernel sums the numerator inside the MFMA and the
+        # normalizer per lane).  A sum of T positive fp32 terms is within (T-1)*2^-24 of
+        # the exact one, relatively, so the quotient is within 2*T*2^-24 of 1.
+        tol = 2 * T * 2.0 ** -24 if dtype == "f32" else 1e-2
+        assert float((got - 1).abs().max()) <= tol, algo
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
