@@ -92,6 +92,10 @@ RAGGED = [
     (1, 2, 1, 33, 256, True),
     (3, 8, 8, 300, 96, True),
     (1, 16, 2, 190, 32, True),
+    (2, 4, 2, 300, 64, False),   # full attention over several 128-row workgroup tiles
+    (1, 2, 2, 1, 32, True),      # one row: a workgroup of padding rows
+    (1, 4, 1, 128, 96, True),    # exactly one 128-row tile
+    (1, 2, 1, 1000, 128, True),  # many key tiles, ragged end
 ]
 
 
