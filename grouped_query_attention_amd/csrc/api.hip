@@ -39,7 +39,7 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
   // an explicit kernel request is checked even for empty tensors, so a zero-size call
   // tells the caller whether that kernel covers the shape
   const bool mfma_ok = dtype == GQA_F32
-                           ? window == 0 && gqa::prefill_f32_mfma_supported(d_h, Hq, Hkv)
+                           ? gqa::prefill_f32_mfma_supported(d_h, Hq, Hkv)
                            : gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
   if (algo == GQA_ALGO_MFMA && !mfma_ok) return GQA_EUNSUPPORTED;
   if (B == 0 || T == 0) return GQA_OK;

@@ -1,5 +1,10 @@
 // prefill_f32_mfma.hip -- fp32 causal GQA prefill on the fp32 matrix cores.
 //
+// With a local window W (the multi-query primer's local attention, section 4.1) row i
+// sees keys i-W+1 .. i only: the stage loop starts at the workgroup's first window
+// start, a wave skips tiles wholly below its rows' windows, and tiles that cross a
+// window edge are masked like diagonal tiles.
+//
 // Same computation as the other prefill kernels (scores = scale * Q K^T, causal mask,
 // softmax over keys, times V; query head h reads K/V head h / (Hq/Hkv)), with fp32
 // inputs kept in fp32: the products run on v_mfma_f32_32x32x2_f32, which multiplies
@@ -51,7 +56,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int T, float scale_log2,
-    int causal) {
+    int causal, int window) {
   using G = F32Geo<D>;
   __shared__ __attribute__((aligned(16))) float Ks[kKeys * G::KStride];
   __shared__ __attribute__((aligned(16))) float Vt[D * kVtStride];
@@ -87,6 +92,11 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
   const int wg_rows_end = min(T, (qt + 1) * kWaves * kRows);
   const int kend = causal ? wg_rows_end : T;
   const int wave_kend = q0 >= T ? 0 : (causal ? min(T, q0 + kRows) : T);
+  // with a window: the first tile any row of the workgroup sees, the first key the wave's
+  // first row sees, and (below it) the first key every row of the wave sees
+  const int kbeg = window > 0 ? max(0, qt * (kWaves * kRows) - window + 1) / kKeys * kKeys : 0;
+  const int wave_kbeg = window > 0 ? q0 - window + 1 : 0;
+  const int wave_kfull = window > 0 ? q0 + kRows - window : 0;
 
   // tile staging: chunk c = threadIdx.x + kThreads*i is key c / C4, head dims 4*(c % C4) ..
   f32x4 kr[G::LPT], vr[G::LPT];
@@ -124,13 +134,13 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
   float m = -INFINITY;  // running max of the lane's query (log2 units), shared by both halves
   float l = 0.f;        // this lane's share of the normalizer (its 16 keys of every tile)
 
-  if (kend > 0) load(0);
-  for (int j0 = 0; j0 < kend; j0 += kKeys) {
+  if (kbeg < kend) load(kbeg);
+  for (int j0 = kbeg; j0 < kend; j0 += kKeys) {
     __syncthreads();  // every wave is done reading the previous tile
     store();
     __syncthreads();
     if (j0 + kKeys < kend) load(j0 + kKeys);  // in flight during this tile's products
-    if (j0 >= wave_kend) continue;            // wave-uniform: no key here is visible
+    if (j0 >= wave_kend || j0 + kKeys <= wave_kbeg) continue;  // wave-uniform: no key visible
 
     f32x16 s;
 #pragma unroll
@@ -144,12 +154,13 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
     }
 
     // mask keys past T and, on the diagonal, keys after the query
-    if (j0 + kKeys > T || (causal && j0 + kKeys - 1 > q0)) {  // wave-uniform
+    if (j0 + kKeys > T || (causal && j0 + kKeys - 1 > q0) || j0 < wave_kfull) {  // wave-uniform
       const int lim = causal ? min(T - 1, qi) : T - 1;  // last key the lane's query sees
+      const int lo = window > 0 ? qi - window + 1 : 0;  // first key it sees
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        s[r] = key <= lim ? s[r] : -INFINITY;
+        s[r] = (key <= lim && key >= lo) ? s[r] : -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -212,7 +223,7 @@ hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_f32_kernel<D>), grid, dim3(kThreads), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), a.out, a.lse, a.Hq, a.Hkv, a.T,
-                     a.scale * 1.4426950408889634f, a.causal);
+                     a.scale * 1.4426950408889634f, a.causal, a.window);
   return hipGetLastError();
 }
 
