@@ -55,7 +55,7 @@ struct F32Geo {
 template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int T, float scale_log2,
+    float* __restrict__ out, float* __restrict__ lse, int B, int Hq, int Hkv, int T, float scale_log2,
     int causal, int window) {
   using G = F32Geo<D>;
   __shared__ __attribute__((aligned(16))) float Ks[kKeys * G::KStride];
@@ -65,9 +65,13 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int h = lane >> 5;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest q-tiles first
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  // one-dimensional grid, heaviest q-tiles first across every (batch, head); the
+  // workgroups of one (batch, head) keep the residue of their id mod 8, and so their
+  // XCD, when B*Hq is a multiple of 8
+  const int units = Hq * B;
+  const int qt = (int)(gridDim.x / units) - 1 - (int)blockIdx.x / units;
+  const int hq = (int)blockIdx.x % units % Hq;
+  const int b = (int)blockIdx.x % units / Hq;
   const int g = hq / (Hq / Hkv);
   const int q0 = qt * (kWaves * kRows) + wave * kRows;  // the wave's first query row
   const int qi = q0 + col;                              // the lane's query row
@@ -219,10 +223,11 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
 
 template <int D>
 hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
-  dim3 grid((a.T + kWaves * kRows - 1) / (kWaves * kRows), a.Hq, a.B);
+  const int nqt = (a.T + kWaves * kRows - 1) / (kWaves * kRows);
+  dim3 grid(nqt * a.Hq * a.B);  // q-tile-major: all (batch, head) pairs of the heaviest tile first
   hipLaunchKernelGGL((prefill_f32_kernel<D>), grid, dim3(kThreads), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                     static_cast<const float*>(a.v), a.out, a.lse, a.Hq, a.Hkv, a.T,
+                     static_cast<const float*>(a.v), a.out, a.lse, a.B, a.Hq, a.Hkv, a.T,
                      a.scale * 1.4426950408889634f, a.causal, a.window);
   return hipGetLastError();
 }
