@@ -32,7 +32,7 @@ __device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((ui
 template <typename T, int DPL>
 __global__ __launch_bounds__(256) void attn_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    float* __restrict__ out, int Hq, int Hkv, int Tq, int Tk, int d, float scale_log2, int causal,
+    float* __restrict__ out, int B, int Hq, int Hkv, int Tq, int Tk, int d, float scale_log2, int causal,
     int pos0, int window, long long q_sb, long long q_sh, long long q_st, float* __restrict__ lse) {
   constexpr int DP = DPL * kLanesPerRow;  // padded head dim held by one row
   __shared__ __attribute__((aligned(16))) float Ks[kKeysPerTile * DP];
@@ -41,10 +41,13 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
   const int tid = threadIdx.x;
   const int r = tid / kLanesPerRow;  // row within the block
   const int c = tid % kLanesPerRow;  // lane within the row
-  const int b = blockIdx.z;
-  const int h = blockIdx.y;
+  // one-dimensional grid: the last row block (the most keys) of every (batch, head) first
+  const int units = Hq * B;
+  const int rb = (int)(gridDim.x / units) - 1 - (int)blockIdx.x / units;
+  const int h = (int)blockIdx.x % units % Hq;
+  const int b = (int)blockIdx.x % units / Hq;
   const int g = h / (Hq / Hkv);
-  const int row0 = blockIdx.x * kRowsPerBlock;
+  const int row0 = rb * kRowsPerBlock;
   const int i = row0 + r;
   const bool row_ok = i < Tq;
   const long long pos = (long long)pos0 + i;  // absolute position of this row
@@ -128,10 +131,11 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
 
 template <typename T, int DPL>
 hipError_t launch_t(const GenericArgs& a, hipStream_t stream) {
-  dim3 grid((a.Tq + kRowsPerBlock - 1) / kRowsPerBlock, a.Hq, a.B);
-  hipLaunchKernelGGL((attn_generic_kernel<T, DPL>), grid, dim3(256), 0, stream,
+  const long long blocks = (long long)((a.Tq + kRowsPerBlock - 1) / kRowsPerBlock) * a.Hq * a.B;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_generic_kernel<T, DPL>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), a.out, a.Hq, a.Hkv, a.Tq, a.Tk, a.d,
+                     static_cast<const T*>(a.v), a.out, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, a.d,
                      a.scale * 1.4426950408889634f, a.causal, a.pos0, a.window, a.q_sb, a.q_sh,
                      a.q_st, a.lse);
   return hipGetLastError();

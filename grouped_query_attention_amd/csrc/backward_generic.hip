@@ -59,14 +59,17 @@ __global__ __launch_bounds__(256) void bwd_gen_dq_kernel(const E* __restrict__ q
                                                          const E* __restrict__ v, const float* __restrict__ dout,
                                                          const float* __restrict__ lse2,
                                                          const float* __restrict__ Dv, float* __restrict__ dq,
-                                                         int Hq, int Hkv, int T, int d, float c, float scale,
+                                                         int B, int Hq, int Hkv, int T, int d, float c, float scale,
                                                          int causal) {
   constexpr int DP = DPL * kLanes;
   __shared__ float Ks[kRows * DP];
   __shared__ float Vs[kRows * DP];
   const int tid = threadIdx.x, r = tid / kLanes, cl = tid % kLanes;
-  const int b = blockIdx.z, h = blockIdx.y, g = h / (Hq / Hkv);
-  const int i = blockIdx.x * kRows + r;
+  // one-dimensional grid: the last row block (the most keys) of every (batch, head) first
+  const int units = Hq * B;
+  const int rb = (int)(gridDim.x / units) - 1 - (int)blockIdx.x / units;
+  const int h = (int)blockIdx.x % units % Hq, b = (int)blockIdx.x % units / Hq, g = h / (Hq / Hkv);
+  const int i = rb * kRows + r;
   const bool row_ok = i < T;
   const long long row = ((long long)b * Hq + h) * T + i;
   const long long kvoff = ((long long)b * Hkv + g) * (long long)T * d;
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void bwd_gen_dq_kernel(const E* __restrict__ q
   const float l2 = row_ok ? lse2[row] : 0.f;
   const float Di = row_ok ? Dv[row] : 0.f;
   // keys the block's rows can see
-  const int kv_lim = causal ? min(T, (int)blockIdx.x * kRows + kRows) : T;
+  const int kv_lim = causal ? min(T, rb * kRows + kRows) : T;
 
   for (int j0 = 0; j0 < kv_lim; j0 += kRows) {
     __syncthreads();
@@ -128,17 +131,20 @@ __global__ __launch_bounds__(256) void bwd_gen_dkdv_kernel(const E* __restrict__
                                                            const float* __restrict__ dout,
                                                            const float* __restrict__ lse2,
                                                            const float* __restrict__ Dv, float* __restrict__ dk,
-                                                           float* __restrict__ dv, int Hq, int Hkv, int T, int d,
-                                                           float c, float scale, int causal) {
+                                                           float* __restrict__ dv, int B, int Hq, int Hkv, int T,
+                                                           int d, float c, float scale, int causal) {
   constexpr int DP = DPL * kLanes;
   __shared__ float Qs[kRows * DP];
   __shared__ float Gs[kRows * DP];
   __shared__ float L2s[kRows];
   __shared__ float Ds[kRows];
   const int tid = threadIdx.x, r = tid / kLanes, cl = tid % kLanes;
-  const int b = blockIdx.z, g = blockIdx.y;
+  // one-dimensional grid: the first key block (the most queries) of every (batch, K/V head) first
+  const int units = Hkv * B;
+  const int kb = (int)blockIdx.x / units;
+  const int g = (int)blockIdx.x % units % Hkv, b = (int)blockIdx.x % units / Hkv;
   const int G = Hq / Hkv;
-  const int j = blockIdx.x * kRows + r;  // this row's key
+  const int j = kb * kRows + r;  // this row's key
   const bool key_ok = j < T;
   const long long krow = ((long long)b * Hkv + g) * T + j;
 
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_gen_dkdv_kernel(const E* __restrict__
     av[u] = 0.f;
   }
   // query rows before the block's first key see none of its keys
-  const int i_beg = causal ? (int)blockIdx.x * kRows : 0;
+  const int i_beg = causal ? kb * kRows : 0;
   for (int hq = g * G; hq < g * G + G; ++hq) {
     const long long qbase = ((long long)b * Hq + hq) * T;
     for (int i0 = i_beg; i0 < T; i0 += kRows) {
@@ -208,13 +214,14 @@ __global__ __launch_bounds__(256) void bwd_gen_dkdv_kernel(const E* __restrict__
 template <typename E, int DPL>
 hipError_t launch_t(const BackwardArgs& a, hipStream_t s) {
   const float c = a.scale * kLog2e;
-  const unsigned nb = (unsigned)((a.T + kRows - 1) / kRows);
-  hipLaunchKernelGGL((bwd_gen_dq_kernel<E, DPL>), dim3(nb, a.Hq, a.B), dim3(256), 0, s,
+  const long long nb = (a.T + kRows - 1) / kRows;
+  if (nb * a.Hq * a.B > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_gen_dq_kernel<E, DPL>), dim3((unsigned)(nb * a.Hq * a.B)), dim3(256), 0, s,
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.dout,
-                     a.lse2, a.Dv, a.dq, a.Hq, a.Hkv, a.T, a.d, c, a.scale, a.causal);
-  hipLaunchKernelGGL((bwd_gen_dkdv_kernel<E, DPL>), dim3(nb, a.Hkv, a.B), dim3(256), 0, s,
+                     a.lse2, a.Dv, a.dq, a.B, a.Hq, a.Hkv, a.T, a.d, c, a.scale, a.causal);
+  hipLaunchKernelGGL((bwd_gen_dkdv_kernel<E, DPL>), dim3((unsigned)(nb * a.Hkv * a.B)), dim3(256), 0, s,
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.dout,
-                     a.lse2, a.Dv, a.dk, a.dv, a.Hq, a.Hkv, a.T, a.d, c, a.scale, a.causal);
+                     a.lse2, a.Dv, a.dk, a.dv, a.B, a.Hq, a.Hkv, a.T, a.d, c, a.scale, a.causal);
   return hipGetLastError();
 }
 
