@@ -44,7 +44,7 @@ struct PrefillArgs {
 };
 bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
-// fp32 matrix-core prefill (the same PrefillArgs, fp32 q/k/v): d in {32, 64, 96, 128}.
+// fp32 matrix-core prefill (the same PrefillArgs, fp32 q/k/v): d a multiple of 16, <= 128.
 bool prefill_f32_mfma_supported(int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_f32_mfma(const PrefillArgs& a, hipStream_t stream);
 

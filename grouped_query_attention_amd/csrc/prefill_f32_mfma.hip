@@ -1,4 +1,5 @@
-// prefill_f32_mfma.hip -- fp32 causal GQA prefill on the fp32 matrix cores.
+// prefill_f32_mfma.hip -- fp32 causal GQA prefill on the fp32 matrix cores.  Head dims are
+// multiples of 16 up to 128; the kernel works on d rounded up to 32, with zero padding.
 //
 // With a local window W (the multi-query primer's local attention, section 4.1) row i
 // sees keys i-W+1 .. i only: the stage loop starts at the workgroup's first window
@@ -56,7 +57,7 @@ struct F32Geo {
 template <int D, int HPW>
 __global__ __launch_bounds__(kWaves * 64 * HPW) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ out, float* __restrict__ lse, int B, int Hq, int Hkv, int T, float scale_log2,
+    float* __restrict__ out, float* __restrict__ lse, int B, int Hq, int Hkv, int T, int d, float scale_log2,
     int causal, int window) {
   using G = F32Geo<D, HPW>;
   constexpr int kThreads = G::Threads;
@@ -78,18 +79,20 @@ __global__ __launch_bounds__(kWaves * 64 * HPW) void prefill_f32_kernel(
   const int g = hq / (Hq / Hkv);
   const int q0 = qt * (kWaves * kRows) + wave % kWaves * kRows;  // the wave's first query row
   const int qi = q0 + col;                              // the lane's query row
-  const long long qbase = ((long long)b * Hq + hq) * (long long)T * D;
-  const long long kvbase = ((long long)b * Hkv + g) * (long long)T * D;
+  // rows in memory are d floats; D is d rounded up to 32, the padded dims are zeros
+  const long long qbase = ((long long)b * Hq + hq) * (long long)T * d;
+  const long long kvbase = ((long long)b * Hkv + g) * (long long)T * d;
 
   // Q^T fragment: head dims h*D/2 .. h*D/2 + D/2 - 1 of the lane's row, times scale*log2(e)
   // so that scores come out in log2 units.  Rows past T are zero (never stored).
   float qf[G::Half];
   {
     const bool ok = qi < T;
-    const float* src = q + qbase + (long long)(ok ? qi : 0) * D + h * G::Half;
+    const float* src = q + qbase + (long long)(ok ? qi : 0) * d + h * G::Half;
 #pragma unroll
     for (int u = 0; u < G::Half / 4; ++u) {
-      f32x4 x = ok ? *reinterpret_cast<const f32x4*>(src + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 x = (ok && h * G::Half + 4 * u < d) ? *reinterpret_cast<const f32x4*>(src + 4 * u)
+                                                : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf[4 * u + e] = x[e] * scale_log2;
     }
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(kWaves * 64 * HPW) void prefill_f32_kernel(
     for (int i = 0; i < G::LPT; ++i) {
       const int c = threadIdx.x + kThreads * i;
       const int j = j0 + c / G::C4;
-      const long long off = kvbase + (long long)j * D + 4 * (c % G::C4);
-      if (j < T) {
+      const int e0 = 4 * (c % G::C4);
+      const long long off = kvbase + (long long)j * d + e0;
+      if (j < T && e0 < d) {
         kr[i] = *reinterpret_cast<const f32x4*>(k + off);
         vr[i] = *reinterpret_cast<const f32x4*>(v + off);
       } else {
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(kWaves * 64 * HPW) void prefill_f32_kernel(
     const float lt = l + __shfl_xor(l, 32);
     if (qi < T) {
       const float inv = 1.f / lt;
-      float* dst = out + qbase + (long long)qi * D;
+      float* dst = out + qbase + (long long)qi * d;
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(kWaves * 64 * HPW) void prefill_f32_kernel(
           f32x4 x;
 #pragma unroll
           for (int u = 0; u < 4; ++u) x[u] = o[db][4 * rr + u] * inv;
-          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * rr + 4 * h) = x;
+          if (32 * db + 8 * rr + 4 * h < d) *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * rr + 4 * h) = x;
         }
       // row log-sum-exp of the scaled scores, natural log
       if (lse && h == 0)
@@ -230,7 +234,7 @@ hipError_t launch_f32h(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid(nqt * (a.Hq / HPW) * a.B);  // q-tile-major: every (batch, head group) of the heaviest tile first
   hipLaunchKernelGGL((prefill_f32_kernel<D, HPW>), grid, dim3(kWaves * 64 * HPW), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                     static_cast<const float*>(a.v), a.out, a.lse, a.B, a.Hq, a.Hkv, a.T,
+                     static_cast<const float*>(a.v), a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, a.d,
                      a.scale * 1.4426950408889634f, a.causal, a.window);
   return hipGetLastError();
 }
@@ -248,15 +252,15 @@ hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool prefill_f32_mfma_supported(int d, int Hq, int Hkv) {
-  return d > 0 && d <= 128 && d % 32 == 0 && Hkv > 0 && Hq % Hkv == 0;
+  return d > 0 && d <= 128 && d % 16 == 0 && Hkv > 0 && Hq % Hkv == 0;
 }
 
 hipError_t launch_attn_prefill_f32_mfma(const PrefillArgs& a, hipStream_t stream) {
-  switch (a.d) {
-    case 32: return launch_f32<32>(a, stream);
-    case 64: return launch_f32<64>(a, stream);
-    case 96: return launch_f32<96>(a, stream);
-    case 128: return launch_f32<128>(a, stream);
+  switch ((a.d + 31) / 32) {  // d a multiple of 16, padded to the next multiple of 32
+    case 1: return launch_f32<32>(a, stream);
+    case 2: return launch_f32<64>(a, stream);
+    case 3: return launch_f32<96>(a, stream);
+    case 4: return launch_f32<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -52,7 +52,7 @@ enum gqa_algo {
     GQA_ALGO_AUTO = 0,    /* fastest kernel built for the shape */
     GQA_ALGO_GENERIC = 1, /* vector-ALU kernel: any d_h in [1, 256], fp32 or bf16 */
     GQA_ALGO_MFMA = 2     /* matrix-core kernel: bf16 with d_h a multiple of 16, <= 128, or
-                             fp32 with d_h a multiple of 32, <= 128 (products in fp32) */
+                             fp32 with d_h a multiple of 16, <= 128 (products in fp32) */
 };
 
 /*

@@ -61,8 +61,8 @@ def prefill(q=A16, k=A16, v=A16, out=A16, B=1, Hq=2, Hkv=1, T=4, d=8, scale=0.5,
     (dict(algo=9), EINVAL),
     (dict(q=None), EINVAL),                 # null pointer for a non-empty tensor
     (dict(out=A16 + 4), EINVAL),            # misaligned
-    (dict(d=8, algo=2, dtype=F32), EUNSUP),  # fp32 matrix-core kernel: d a multiple of 32
-    (dict(d=48, algo=2, dtype=F32), EUNSUP),
+    (dict(d=8, algo=2, dtype=F32), EUNSUP),  # fp32 matrix-core kernel: d a multiple of 16
+    (dict(d=40, algo=2, dtype=F32), EUNSUP),
     (dict(d=160, algo=2, dtype=F32), EUNSUP),  # and at most 128
     (dict(d=8, algo=2), EUNSUP),            # d not a multiple of 16
 ])
