@@ -114,6 +114,17 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A new tensor for the library to write on `stream`.  It is allocated with that
+    stream current, so torch's caching allocator hands its block out again only in that
+    stream's order: a workspace dropped on return, or an output the caller frees, is
+    never reused by another stream while the kernels may still write it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def attn_prefill(q, k, v, scale=None, causal=True, out=None, algo=GQA_ALGO_AUTO, stream=None,
                  window=None):
     """Causal (or full) GQA prefill.  q [B,Hq,T,d]; k, v [B,Hkv,T,d] (same dtype,
@@ -129,7 +140,7 @@ def attn_prefill(q, k, v, scale=None, causal=True, out=None, algo=GQA_ALGO_AUTO,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, Hq, T, d), torch.float32, q.device, stream)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
     if window is not None:
@@ -178,7 +189,7 @@ def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, s
     Hkv, L = kcache.shape[1], kcache.shape[2]
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, n, Hq, d), torch.float32, q.device, stream)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
     if window is None:
@@ -186,7 +197,7 @@ def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, s
     else:
         need = attn_decode_window_workspace_bytes(B, n, L, Hq, Hkv, d, window, dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if window is None:
@@ -238,7 +249,7 @@ def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspac
     max_blocks = block_table.shape[1]
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, n, Hq, d), torch.float32, q.device, stream)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
     if window is None:
@@ -246,7 +257,7 @@ def attn_decode_paged(q, kpool, vpool, block_table, seq_lens, out=None, workspac
     else:
         need = attn_decode_paged_window_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, window, dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ptrs = (_dev_ptr(q, "q"), _dev_ptr(kpool, "kpool"), _dev_ptr(vpool, "vpool"),
@@ -284,12 +295,12 @@ def attn_decode_blocks(q, kpool, vpool, block_table, seq_lens, out=None, workspa
     max_blocks = block_table.shape[1]
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, n, Hq, d), torch.float32, q.device, stream)
     elif out.shape != q.shape or out.dtype != torch.float32:
         raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
     need = attn_decode_paged_workspace_bytes(B, n, Hq, Hkv, d, bs, max_blocks, dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.attn_decode_blocks(_dev_ptr(q, "q"), _dev_ptr(kpool, "kpool"), _dev_ptr(vpool, "vpool"),
@@ -369,9 +380,9 @@ def attn_prefill_lse(q, k, v, scale=None, causal=True, out=None, lse=None, strea
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, Hq, T, d), torch.float32, q.device, stream)
     if lse is None:
-        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq, T), torch.float32, q.device, stream)
     if out.shape != q.shape or out.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, T) \
             or lse.dtype != torch.float32:
         raise ValueError("out must be float32 like q and lse float32 [B, Hq, T]")
@@ -404,12 +415,15 @@ def attn_backward(q, k, v, out, dout, lse, scale=None, causal=True, dq=None, dk=
         raise ValueError("lse must be float32 [B, Hq, T]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device) if dq is None else dq
-    dk = torch.empty((B, Hkv, T, d), dtype=torch.float32, device=q.device) if dk is None else dk
-    dv = torch.empty((B, Hkv, T, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    dq = _empty((B, Hq, T, d), torch.float32, q.device, stream) if dq is None else dq
+    dk = _empty((B, Hkv, T, d), torch.float32, q.device, stream) if dk is None else dk
+    dv = _empty((B, Hkv, T, d), torch.float32, q.device, stream) if dv is None else dv
+    for t, n, shape in ((dq, "dq", (B, Hq, T, d)), (dk, "dk", (B, Hkv, T, d)), (dv, "dv", (B, Hkv, T, d))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32:
+            raise ValueError("%s must be float32 of shape %s; got %s %s" % (n, shape, t.dtype, tuple(t.shape)))
     need = attn_backward_workspace_bytes(B, Hq, Hkv, T, d, _dtype_code(q))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.attn_backward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),

@@ -12,7 +12,8 @@ namespace {
 
 constexpr int kMaxHeadDim = 256;
 constexpr long long kMaxSeq = 1LL << 30;
-constexpr int kMaxGridYZ = 65535;
+// every grid is one-dimensional and decodes (batch, head) from a 32-bit block index
+constexpr long long kMaxBatchHeads = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -21,7 +22,7 @@ int check_common(int dtype, int B, int Hq, int Hkv, int d_h) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || d_h <= 0) return GQA_EINVAL;
   if (Hq % Hkv != 0) return GQA_EINVAL;
   if (d_h > kMaxHeadDim) return GQA_EUNSUPPORTED;
-  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return GQA_EUNSUPPORTED;
+  if ((long long)B * Hq > kMaxBatchHeads) return GQA_EUNSUPPORTED;
   return GQA_OK;
 }
 

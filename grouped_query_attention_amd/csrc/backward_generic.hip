@@ -245,7 +245,7 @@ hipError_t launch_attn_backward_generic(BackwardArgs a, void* workspace, int dty
   a.lse2 = reinterpret_cast<float*>(ws);
   a.Dv = reinterpret_cast<float*>(ws + fb);
   const long long pb = (rows + 3) / 4;
-  if (pb > 0x7fffffffLL || a.B > 65535 || a.Hq > 65535) return hipErrorInvalidValue;
+  if (pb > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_gen_prep_kernel, dim3((unsigned)pb), dim3(256), 0, stream, a.out, a.dout, a.lse,
                      a.lse2, a.Dv, rows, a.d);
   return dtype == kF32 ? launch_dt<float>(a, stream) : launch_dt<uint16_t>(a, stream);

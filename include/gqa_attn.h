@@ -91,7 +91,10 @@ int attn_prefill_window(const void* q, const void* k, const void* v, float* out,
 /*
  * Bytes of device workspace attn_decode_cached needs for this shape (0 when it needs
  * none).  Pure host arithmetic; the same arguments always give the same answer.
- * Returns 0 for arguments attn_decode_cached would reject.
+ * Returns 0 for arguments attn_decode_cached would reject.  dtype is an argument
+ * because the plan depends on it: a bf16 cache runs the split-KV matrix-core kernels,
+ * whose chunk partials live in the workspace; an fp32 cache runs the vector kernel,
+ * which needs none.
  */
 size_t attn_decode_workspace_bytes(int B, int newTokens, int totalLen, int Hq, int Hkv, int d_h,
                                    int dtype);
@@ -153,8 +156,8 @@ size_t attn_decode_paged_workspace_bytes(int B, int newTokens, int Hq, int Hkv, 
 
 /*
  * Paged (block-table) cached decode: makarna's CausalAttentionPackedBlocks, and the
- * "paged decode attention" of the Hesper-style backend notes (one new-token query
- * block reading a logical-to-physical K/V page table).  Per sequence b it computes
+ * "paged decode attention" of Riftco's "Algorithm and cache boundaries" section (the
+ * one-query inference algorithm reading a logical-to-physical K/V page table).  Per sequence b it computes
  * exactly attn_decode_cached over the history its blocks hold.
  *
  *   q, out          : [B, newTokens, Hq, d_h]  as in attn_decode_cached

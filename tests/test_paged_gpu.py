@@ -2,7 +2,7 @@
 
 attn_decode_paged reads each sequence's K/V history out of a fragmented block pool
 through a block table (makarna's CausalAttentionPackedBlocks; the "paged decode
-attention" of the Hesper-style backend notes).  Checked here:
+attention" of Riftco's "Algorithm and cache boundaries").  Checked here:
 
 * element-wise parity with oracle.decode_paged on ragged lengths (length = newTokens,
   block boundaries, several key chunks), block sizes 16..256 including 48, head dims
