@@ -19,7 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgqa_attn.so")
 
 GQA_F32, GQA_BF16 = 0, 1
-GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_EHIP = 0, -1, -2, -3, -4
+GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_EHIP, GQA_ESCRATCH = 0, -1, -2, -3, -4, -5
+GQA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed scratch of attn_decode_cached_noalloc
 GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
 
 # every symbol include/gqa_attn.h declares
@@ -29,7 +30,7 @@ EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_prefill_window", "attn_deco
             "attn_decode_paged_window_workspace_bytes", "attn_decode_paged_window", "attn_decode_blocks",
             "attn_kv_append",
             "attn_kv_append_paged", "attn_prefill_lse", "attn_backward_workspace_bytes", "attn_backward",
-            "attn_strerror")
+            "attn_strerror", "attn_decode_cached_noalloc")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgqa_attn.so is not built (%s); run python grouped_query_attention_amd/build.py"
@@ -78,6 +79,8 @@ lib.attn_backward_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 lib.attn_backward.restype = _i
 lib.attn_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
                               _vp, _sz, _vp]
+lib.attn_decode_cached_noalloc.restype = _i
+lib.attn_decode_cached_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
@@ -212,6 +215,29 @@ def attn_decode_cached(q, kcache, vcache, start_pos, out=None, workspace=None, s
         what = "attn_decode_window"
     if rc != GQA_OK:
         raise GQAError(rc, what)
+    return out
+
+
+def attn_decode_cached_noalloc(q, kcache, vcache, start_pos, out, stream=None):
+    """attn_decode_cached without a workspace: the library keeps the split-KV partials in
+    its fixed device scratch (GQA_NOALLOC_SCRATCH_BYTES per GPU), so the call allocates
+    nothing.  out [B,n,Hq,d] float32 must be supplied.  Calls that overlap on one GPU
+    share the scratch and race; shapes needing more scratch raise GQAError with
+    GQA_ESCRATCH."""
+    B, n, Hq, d = q.shape
+    if kcache.dim() != 4 or kcache.shape[0] != B or kcache.shape[3] != d or vcache.shape != kcache.shape:
+        raise ValueError("kcache, vcache must be [B, Hkv, L, d]; got %s %s"
+                         % (tuple(kcache.shape), tuple(vcache.shape)))
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise TypeError("q, kcache, vcache must share one dtype")
+    if out is None or out.shape != q.shape or out.dtype != torch.float32:
+        raise ValueError("out must be float32 of shape %s" % (tuple(q.shape),))
+    Hkv, L = kcache.shape[1], kcache.shape[2]
+    rc = lib.attn_decode_cached_noalloc(_dev_ptr(q, "q"), _dev_ptr(kcache, "kcache"), _dev_ptr(vcache, "vcache"),
+                                        _dev_ptr(out, "out"), n, L, int(start_pos), Hq, Hkv, d, B,
+                                        _dtype_code(q), _stream_handle(stream, q.device))
+    if rc != GQA_OK:
+        raise GQAError(rc, "attn_decode_cached_noalloc")
     return out
 
 

@@ -360,6 +360,7 @@ const char* attn_strerror(int code) {
     case GQA_EUNSUPPORTED: return "unsupported shape or dtype for the built kernels";
     case GQA_EWORKSPACE: return "decode workspace missing or too small";
     case GQA_EHIP: return "HIP runtime error at launch";
+    case GQA_ESCRATCH: return "shape needs more than the fixed scratch of attn_decode_cached_noalloc";
     default: return "unknown status code";
   }
 }

@@ -44,8 +44,14 @@ enum gqa_status {
     GQA_EINVAL = -1,       /* argument outside the documented domain */
     GQA_EUNSUPPORTED = -2, /* valid, but no kernel is built for it (e.g. d_h > 256) */
     GQA_EWORKSPACE = -3,   /* decode workspace missing or too small */
-    GQA_EHIP = -4          /* the HIP runtime reported an error at launch */
+    GQA_EHIP = -4,         /* the HIP runtime reported an error at launch */
+    GQA_ESCRATCH = -5      /* the shape needs more than the fixed scratch of
+                              attn_decode_cached_noalloc (GQA_NOALLOC_SCRATCH_BYTES) */
 };
+
+/* Size of the fixed device scratch array attn_decode_cached_noalloc keeps its split-KV
+ * partials in (one copy per GPU the library runs on, held until the process ends). */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Kernel selection for attn_prefill_ex (attn_prefill always uses GQA_ALGO_AUTO). */
 enum gqa_algo {
@@ -128,6 +134,33 @@ int attn_decode_num_splits(int B, int newTokens, int totalLen, int Hq, int Hkv, 
 int attn_decode_cached(const void* q, const void* kcache, const void* vcache, float* out,
                        int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h, int B,
                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_cached for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It computes
+ * exactly what attn_decode_cached does (same kernels, same split plan, bitwise the same
+ * result), but keeps the split-KV partials in a fixed device array of
+ * GQA_NOALLOC_SCRATCH_BYTES inside the library instead of a caller workspace.  The
+ * caller still passes q, the caches and out.  It never calls hipMalloc, hipFree or any
+ * allocating routine; the first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress) and keeps its address.
+ *
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (different streams, or different threads, without ordering between them) race and
+ * may corrupt each other's results; serialize them.  Nothing in the array needs to
+ * start at zero: every partial a call reads was written earlier in the same call.
+ * The array keeps the last call's partials.
+ *
+ * Arguments as attn_decode_cached without the workspace.  Errors as
+ * attn_decode_cached, plus GQA_ESCRATCH, returned before anything is enqueued, when
+ * attn_decode_workspace_bytes(...) for the shape exceeds GQA_NOALLOC_SCRATCH_BYTES
+ * (e.g. 64 or more new tokens for 64 sequences of 32 query heads over a 32768-position
+ * history at d_h = 128; up to 63 fit), and GQA_EHIP when the current device or the
+ * array's address cannot be obtained.
+ */
+int attn_decode_cached_noalloc(const void* q, const void* kcache, const void* vcache, float* out,
+                               int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h,
+                               int B, int dtype, void* stream);
 
 /*
  * Local-window cached decode: attn_decode_cached where new token i (position
