@@ -140,10 +140,10 @@ def test_backward_rejects(gqa):
         gqa.attn_backward(q, k, k, o, o, lse, workspace=small)
 
 
-def test_full_size_backward_sampled_groups(gqa):
+def test_full_size_backward_every_group(gqa):
     """The GQA prefill workload (B=2, 16 query / 8 K/V heads, T=4096, d=128, bf16) in the
-    launch configuration the benchmark times; two sampled (batch, K/V head) groups checked
-    in full against the oracle restricted to that group."""
+    launch configuration the benchmark times; every (batch, K/V head) group checked in
+    full against the oracle restricted to that group (max-abs and max-rel printed)."""
     cfg = si.GQA_T4096
     q, k, v = si.prefill_config_inputs(cfg)
     g = torch.Generator().manual_seed(cfg.seed + 100)
@@ -153,14 +153,25 @@ def test_full_size_backward_sampled_groups(gqa):
     dq, dk, dv = gqa.attn_backward(qd, kd, vd, out, dout.cuda(), lse, scale=cfg.scale, causal=True)
     torch.cuda.synchronize()
     G = cfg.Hq // cfg.Hkv
-    for b, gk in ((0, 0), (1, cfg.Hkv - 1)):
-        hs = slice(gk * G, (gk + 1) * G)
-        wq, wk, wv = bw.backward(q[b:b + 1, hs].double().numpy(), k[b:b + 1, gk:gk + 1].double().numpy(),
-                                 v[b:b + 1, gk:gk + 1].double().numpy(), dout[b:b + 1, hs].double().numpy(),
-                                 cfg.scale, True)
-        close(dq[b:b + 1, hs], wq)
-        close(dk[b:b + 1, gk:gk + 1], wk)
-        close(dv[b:b + 1, gk:gk + 1], wv)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    stats = {n: [0.0, 0.0, 0.0] for n in ("dq", "dk", "dv")}  # max-abs, max |ref|, max-rel
+    for b in range(cfg.B):
+        print("backward oracle, batch %d" % b, flush=True)
+        for gk in range(cfg.Hkv):
+            hs = slice(gk * G, (gk + 1) * G)
+            wq, wk, wv = bw.backward(q[b:b + 1, hs].double().numpy(), k[b:b + 1, gk:gk + 1].double().numpy(),
+                                     v[b:b + 1, gk:gk + 1].double().numpy(), dout[b:b + 1, hs].double().numpy(),
+                                     cfg.scale, True)
+            for n, got, want in (("dq", dq[b:b + 1, hs], wq), ("dk", dk[b:b + 1, gk:gk + 1], wk),
+                                 ("dv", dv[b:b + 1, gk:gk + 1], wv)):
+                close(got, want)
+                diff = np.abs(got.double().numpy() - want)
+                st = stats[n]
+                st[0] = max(st[0], float(diff.max()))
+                st[1] = max(st[1], float(np.abs(want).max()))
+                st[2] = max(st[2], float((diff / np.maximum(np.abs(want), 1.0)).max()))
+    for n, (ma, mref, mrel) in stats.items():
+        print("full-size %s: max-abs %.3g, max |ref| %.3g, max-abs / max(1, |ref|) %.3g" % (n, ma, mref, mrel))
 
 
 GEN_CASES = [
