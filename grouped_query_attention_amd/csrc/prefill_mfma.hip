@@ -35,8 +35,13 @@
 //    primer's local attention, section 4.1: keys p-W+1 .. p) skips from both sides:
 //    stages below the workgroup's first window start are never loaded, blocks below a
 //    wave's window are not computed, and window-edge blocks are masked.
-//  * Heaviest q-tiles are dispatched first; blocks of one (batch, head group) keep
-//    the same block-id residue mod 8, i.e. stay on one XCD and share its L2.
+//  * Dispatch order: (batch, head group) units in chunks sized so that one round of
+//    resident workgroups covers every q-tile of a chunk, heaviest q-tiles first inside
+//    a chunk; blocks of one unit keep the same block-id residue mod 8, i.e. stay on one
+//    XCD and share its L2.
+//  * Head dims that are 16 mod 32 (the P V product runs over the next multiple of 32):
+//    the first padded V column in LDS holds ones, so the normalizer accumulates in the
+//    numerator's row D on the matrix core instead of in vector sums.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,8 +76,8 @@ struct Geo {
   // V rows: per bank cycle (64 banks x 4 bytes) the transposed reads of 32 lanes touch
   // 4 consecutive rows x 64 bytes; a row stride of 64 or 192 mod 256 bytes puts those
   // 4 rows in distinct banks (measured conflict-free; 32 mod 128 is not).  Rows are
-  // read up to the next multiple of 32 head dims (the padding feeds discarded O^T rows
-  // only).
+  // read up to the next multiple of 32 head dims; the padding feeds discarded O^T rows,
+  // except that for head dims 16 mod 32 its first column holds ones (the normalizer).
   static constexpr int kVRead = 64 * kDBlocks;
   static constexpr int kVStride = (kVRead % 256 <= 64) ? kVRead - kVRead % 256 + 64
                                   : (kVRead % 256 <= 192) ? kVRead - kVRead % 256 + 192
@@ -97,8 +102,12 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int Hq, int Hkv, int T, float c,
     unsigned qsign, int causal, int window_arg, int n_qtiles, int n_hgroups, int B,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int chunk_units) {
   using G_ = Geo<D>;
+  // Head dims 16 mod 32: the P V product runs over the next multiple of 32, and the
+  // first padded V column holds ones, so the numerator's row D accumulates the
+  // normalizer (with every rescale applied to it as to the numerator).
+  constexpr bool kOnesCol = D % 32 == 16;
   // the local window is a separate instantiation: plain causal attention carries none
   // of its checks
   const int window = WIN ? window_arg : 0;
@@ -117,11 +126,18 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   const int half = lane >> 5;   // which 16-key half of each 32 the lane holds
   const int col = lane & 31;    // query column of the lane in its wave's 32 rows
 
-  // block -> (q-tile, head group, batch): heaviest q-tiles first
-  const int per_qt = n_hgroups * B;
+  // block -> (q-tile, head group, batch).  Units (batch, head group) are taken in
+  // chunks of chunk_units, every q-tile of a chunk before the next chunk, heaviest
+  // q-tiles first inside a chunk: the workgroups in flight then cover all q-tiles of a
+  // few units, whose K/V stay in L2 (blocks of a unit share their residue mod 8 when
+  // chunk_units is a multiple of 8, so they run on one XCD).
+  const int units = n_hgroups * B;
   const int bid = blockIdx.x;
-  const int qt = n_qtiles - 1 - bid / per_qt;
-  const int rem = bid % per_qt;
+  const int chunk = bid / (chunk_units * n_qtiles);
+  const int in_chunk = min(chunk_units, units - chunk * chunk_units);
+  const int bid_in = bid - chunk * chunk_units * n_qtiles;
+  const int qt = n_qtiles - 1 - bid_in / in_chunk;
+  const int rem = chunk * chunk_units + bid_in % in_chunk;
   const int hg = rem % n_hgroups;
   const int b = rem / n_hgroups;
   const int h = hg * HPW + wave / SLICES;
@@ -169,6 +185,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   constexpr int KI = (kSub * KP + kWgWaves - 1) / kWgWaves;  // wave instructions per wave per stage
   constexpr int VI = (kSub * VP + kWgWaves - 1) / kWgWaves;
   int koff[KI], voff[VI];
+  bool vpad[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
     const int p = (wave + kWgWaves * i) * 64 + lane, cc = p % KP;
@@ -178,6 +195,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   for (int i = 0; i < VI; ++i) {
     const int p = (wave + kWgWaves * i) * 64 + lane, cc = p % VP;
     voff[i] = (p / VP) * RB + (cc < C16 ? cc : 0) * 16;
+    vpad[i] = cc >= C16;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // clamp a source offset to the last valid row of a ragged stage
@@ -203,7 +221,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int inst = wave_u + kWgWaves * i;
-      if (inst < kSub * VP) {
+      if (inst < kSub * VP && !(kOnesCol && vpad[i])) {
         const int off = ragged ? clamp_row(voff[i], rmax) : voff[i];
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(vb + off),
@@ -272,7 +290,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   // by more than kLazyTau), rescale the normalizer, and form p = 2^(s*c - m) in bf16.
   // Returns whether any lane moved its max; the numerator must then be scaled by
   // `alpha` before this block's P V is added.
-  auto softmax_blk = [&](const f32x16& s, bf16x8 (&pb)[2], float& alpha) -> bool {
+  auto softmax_blk = [&](const f32x16& s, bf16x8 (&pb)[2], float& m_old, float& lsum) -> bool {
     // NaN-propagating maximum lowers to v_maximum3_f32 with no operand
     // canonicalization (fmaxf would add one v_max per score)
     float mx = __builtin_elementwise_maximum(s[0], s[1]);
@@ -282,35 +300,42 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     mx = pair_max(mx);
     const float mt = mx * c;  // block max in log2 units
     const bool need = mt > m_run + kLazyTau;
-    // lanes that keep their max keep their scale: exp2(m - m) would be NaN for a
-    // column that has seen only masked keys (m = -inf)
-    alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+    m_old = m_run;
     m_run = need ? mt : m_run;
-    l_part *= alpha;
-    // p, rounded to bf16 for the P V product; the normalizer sums the same bf16
-    // values, two per v_dot2_f32_bf16 against (1, 1).  Under a window a column can
-    // meet a block entirely below its window before any visible key (m = -inf): 0 is
-    // then the reference, and its p are exact zeros.
+    // p, rounded to bf16 for the P V product.  Under a window a column can meet a
+    // block entirely below its window before any visible key (m = -inf): 0 is then the
+    // reference, and its p are exact zeros.
     const float m_ref = (WIN && m_run == -INFINITY) ? 0.f : m_run;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float ls[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         pb[kk][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + e], c, -m_ref));
+    if constexpr (!kOnesCol) {
+      // the normalizer sums the same bf16 values, two per v_dot2_f32_bf16 against (1, 1)
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pb[kk][e], pb[kk][e + 1]};
-        ls[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[kk], false);
-      }
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pb[kk][e], pb[kk][e + 1]};
+          ls[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[kk], false);
+        }
+      lsum = ls[0] + ls[1];
     }
-    l_part += ls[0] + ls[1];
     return __any(need);
   };
-  auto rescale_o = [&](float alpha) {
+  // A block moved the max of some columns (rare with the lazy threshold): scale the
+  // numerator by 2^(m_old - m_new) and return the factor, by which the caller scales
+  // the normalizer of the earlier blocks before adding this block's sum.  Columns that
+  // kept their max keep their scale (2^(m - m) would be NaN for a column that has seen
+  // only masked keys, m = -inf).
+  auto rescale_o = [&](float m_old) {
+    const float alpha = m_old == m_run ? 1.f : __builtin_amdgcn_exp2f(m_old - m_run);
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    return alpha;
   };
 
   // P V of an interior stage's last block, deferred past the stage barrier (its V
@@ -339,9 +364,9 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       bf16x8 vf[2][DB];
       if (b + 1 < kNB) read_k(kl + (b + 1) * kBlk * G_::kKStride, kf);
       if (b >= 1) read_v(vl + (b - 1) * kBlk * G_::kVStride, vf);
-      float alpha;
+      float m_old, lsum = 0.f;
       if constexpr (kMasked) mask_blk(s[b], k0s + b * kBlk);
-      const bool resc = softmax_blk(s[b], pb[b], alpha);
+      const bool resc = softmax_blk(s[b], pb[b], m_old, lsum);
       if (b + 1 < kNB) mfma_s(kf, s[b + 1]);
       if (b >= 1) mfma_pv(vf, pb[b - 1]);
       // interleave: K reads, the max (vector ops), then one matrix op per four vector
@@ -354,7 +379,11 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         if (i >= 3 && i < 11) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      if (resc) rescale_o(alpha);  // after P V of block b-1, before that of block b
+      if (resc) {  // after P V of block b-1, before that of block b
+        const float a = rescale_o(m_old);
+        if constexpr (!kOnesCol) l_part *= a;
+      }
+      if constexpr (!kOnesCol) l_part += lsum;
     }
     read_v(vl + (kNB - 1) * kBlk * G_::kVStride, pend_v);
 #pragma unroll
@@ -386,8 +415,12 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       mfma_s(kf, s);
       if (diag) mask_blk(s, k0);
       bf16x8 pb[2];
-      float alpha;
-      if (softmax_blk(s, pb, alpha)) rescale_o(alpha);
+      float m_old, lsum = 0.f;
+      if (softmax_blk(s, pb, m_old, lsum)) {
+        const float a = rescale_o(m_old);
+        if constexpr (!kOnesCol) l_part *= a;
+      }
+      if constexpr (!kOnesCol) l_part += lsum;
       bf16x8 vf[2][DB];
       read_v(vl + b * kBlk * G_::kVStride, vf);
       mfma_pv(vf, pb);
@@ -419,6 +452,19 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     if (t + 2 < nstages) stage(t + 2, cur);
   };
 
+  if constexpr (kOnesCol) {
+    // the padded V chunks read by the P V product: (1, 0, ..., 0) then zeros, in every
+    // row of both stage arrays; the stage loads never write them
+    constexpr int kPadChunks = G_::kVRead / 16 - C16;
+    for (int i = tid; i < 2 * kStage * kPadChunks; i += kWgWaves * 64) {
+      const int arr = i / (kStage * kPadChunks), rem = i % (kStage * kPadChunks);
+      const int row = rem / kPadChunks, ch = rem % kPadChunks;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (ch == 0) val[0] = 0x3f80u;  // bf16 1.0 in the low half: head dim D
+      char* base = (arr == 0 ? lds_a : lds_b) + G_::kKTile + row * G_::kVStride + (C16 + ch) * 16;
+      *reinterpret_cast<u32x4*>(base) = val;
+    }
+  }
   stage(t0, lds_a);
   if (t0 + 1 < nstages) stage(t0 + 1, lds_b);
   __builtin_amdgcn_s_waitcnt(0);
@@ -430,7 +476,9 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   if (pending) mfma_pv(pend_v, pend_p);
   // epilogue: O^T row (head dim) of accumulator r in block db is
   // 32*db + 8*(r/4) + 4*half + r%4; column is this lane's query.
-  const float l_row = pair_sum(l_part);
+  // accumulator r = 8 of the last block holds head dim 32*(DB-1) + 16 = D in the lanes
+  // of half 0 (the ones column) and D + 4 (a zero column) in half 1
+  const float l_row = pair_sum(kOnesCol ? o[DB - 1][8] : l_part);
   const float inv = 1.f / l_row;
   // row log-sum-exp of the scaled scores, natural log: (m + log2 l) * ln 2 (m is the
   // reference the p were taken against, in log2 units)
@@ -452,6 +500,14 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   }
 }
 
+// Units per chunk of the dispatch order: about one round of resident workgroups (one
+// per CU) covers every q-tile of a chunk's units; at least 32 units, a multiple of 8.
+int chunk_units(int n_qtiles, int units) {
+  int c = 256 / n_qtiles / 8 * 8;
+  if (c < 32) c = 32;
+  return c < units ? c : units;
+}
+
 template <int D, int HPW, bool WIN>
 hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   constexpr int QT = 32 * (kWgWaves / HPW);
@@ -467,7 +523,8 @@ hipError_t launch_dh(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_mfma_kernel<D, HPW, WIN>), dim3((unsigned)nblocks), dim3(kWgWaves * 64), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.out, a.Hq, a.Hkv, a.T, c, qsign, a.causal,
-                     a.causal ? a.window : 0, n_qtiles, n_hgroups, a.B, a.lse);
+                     a.causal ? a.window : 0, n_qtiles, n_hgroups, a.B, a.lse,
+                     chunk_units(n_qtiles, n_hgroups * a.B));
   return hipGetLastError();
 }
 
