@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libgqa_attn.so")
 GQA_F32, GQA_BF16 = 0, 1
 GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_EHIP, GQA_ESCRATCH = 0, -1, -2, -3, -4, -5
 GQA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed scratch of attn_decode_cached_noalloc
-GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA = 0, 1, 2
+GQA_ALGO_AUTO, GQA_ALGO_GENERIC, GQA_ALGO_MFMA, GQA_ALGO_MFMA_SPLIT = 0, 1, 2, 3
 
 # every symbol include/gqa_attn.h declares
 EXPORTED = ("attn_prefill", "attn_prefill_ex", "attn_prefill_window", "attn_decode_workspace_bytes",

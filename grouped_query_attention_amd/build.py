@@ -20,7 +20,8 @@ LIB_NAME = "libgqa_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.hip", "attn_generic.hip", "prefill_mfma.hip", "decode_mfma.hip", "kv_append.hip",
-           "backward_mfma.hip", "backward_generic.hip", "prefill_f32_mfma.hip", "decode_noalloc.hip"]
+           "backward_mfma.hip", "backward_generic.hip", "prefill_f32_mfma.hip", "decode_noalloc.hip",
+           "prefill_small.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.

@@ -14,6 +14,7 @@ constexpr int kMaxHeadDim = 256;
 constexpr long long kMaxSeq = 1LL << 30;
 // every grid is one-dimensional and decodes (batch, head) from a 32-bit block index
 constexpr long long kMaxBatchHeads = 0x7fffffffLL;
+constexpr int kCUs = 256;  // compute units of the MI355X
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -35,7 +36,9 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
   if (rc != GQA_OK) return rc;
   if (T < 0 || !isfinite(scale) || (causal != 0 && causal != 1)) return GQA_EINVAL;
   if (window < 0 || (window > 0 && !causal)) return GQA_EINVAL;
-  if (algo != GQA_ALGO_AUTO && algo != GQA_ALGO_GENERIC && algo != GQA_ALGO_MFMA) return GQA_EINVAL;
+  if (algo != GQA_ALGO_AUTO && algo != GQA_ALGO_GENERIC && algo != GQA_ALGO_MFMA &&
+      algo != GQA_ALGO_MFMA_SPLIT)
+    return GQA_EINVAL;
   if (T > kMaxSeq) return GQA_EUNSUPPORTED;
   // an explicit kernel request is checked even for empty tensors, so a zero-size call
   // tells the caller whether that kernel covers the shape
@@ -43,19 +46,30 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
                            ? gqa::prefill_f32_mfma_supported(d_h, Hq, Hkv)
                            : gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
   if (algo == GQA_ALGO_MFMA && !mfma_ok) return GQA_EUNSUPPORTED;
+  // the split-key kernel: bf16, no local window
+  const bool split_ok = dtype == GQA_BF16 && mfma_ok && (window == 0 || window >= T);
+  if (algo == GQA_ALGO_MFMA_SPLIT && !split_ok) return GQA_EUNSUPPORTED;
   if (B == 0 || T == 0) return GQA_OK;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_EINVAL;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // a window reaching back to key 0 from every row is plain causal attention: take the
+  // same kernel, so the two calls agree bit for bit
+  if (window >= T) window = 0;
+  gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window, lse};
+  // automatic choice: the split-key kernel when one workgroup per q-tile would leave
+  // CUs idle (fewer workgroups than the 256 CUs)
+  if (algo == GQA_ALGO_MFMA_SPLIT ||
+      (algo == GQA_ALGO_AUTO && split_ok && gqa::prefill_mfma_grid(B, Hq, Hkv, T) < kCUs))
+    return status_of(gqa::launch_attn_prefill_small(a, s));
   if (algo == GQA_ALGO_MFMA || (algo == GQA_ALGO_AUTO && mfma_ok)) {
-    gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window, lse};
     if (dtype == GQA_F32) return status_of(gqa::launch_attn_prefill_f32_mfma(a, s));
     return status_of(gqa::launch_attn_prefill_mfma(a, s));
   }
   const long long sd = d_h;
-  gqa::GenericArgs a{q, k, v, out, dtype, B, Hq, Hkv, T, T, d_h, scale, causal, 0,
-                     (long long)Hq * T * sd, (long long)T * sd, sd, window, lse};
-  return status_of(gqa::launch_attn_generic(a, s));
+  gqa::GenericArgs ga{q, k, v, out, dtype, B, Hq, Hkv, T, T, d_h, scale, causal, 0,
+                      (long long)Hq * T * sd, (long long)T * sd, sd, window, lse};
+  return status_of(gqa::launch_attn_generic(ga, s));
 }
 
 bool aligned4(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

@@ -44,6 +44,12 @@ struct PrefillArgs {
 };
 bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+// Workgroups prefill_mfma launches for the shape: fewer than the CU count leaves the
+// chip partly idle, and the split-key kernel below serves such shapes.
+long long prefill_mfma_grid(int B, int Hq, int Hkv, int T);
+// bf16 matrix-core prefill with each 32-row slice's keys split over the waves of its
+// workgroup (no local window); same shapes as prefill_mfma.
+hipError_t launch_attn_prefill_small(const PrefillArgs& a, hipStream_t stream);
 // fp32 matrix-core prefill (the same PrefillArgs, fp32 q/k/v): d a multiple of 16, <= 128.
 bool prefill_f32_mfma_supported(int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_f32_mfma(const PrefillArgs& a, hipStream_t stream);

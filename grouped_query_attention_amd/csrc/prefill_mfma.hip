@@ -538,6 +538,12 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+long long prefill_mfma_grid(int B, int Hq, int Hkv, int T) {
+  const int hpw = (Hq / Hkv) % 2 == 0 ? 2 : 1;
+  const int qt = 32 * (kWgWaves / hpw);
+  return (long long)((T + qt - 1) / qt) * (Hq / hpw) * B;
+}
+
 bool prefill_mfma_supported(int dtype, int d, int Hq, int Hkv) {
   return dtype == kBF16 && d > 0 && d <= 128 && d % 16 == 0 && Hkv > 0 && Hq % Hkv == 0;
 }

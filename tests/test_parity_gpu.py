@@ -34,20 +34,27 @@ def run_prefill(gqa, q, k, v, scale, causal, algo):
     return out
 
 
-ALGOS = {"generic": 1, "mfma": 2}
+ALGOS = {"generic": 1, "mfma": 2, "split": 3}
+
+
+def covers(gqa, dtype, d, algo, Hq=1, Hkv=1):
+    # a zero-size call with an explicit kernel request reports whether it covers the shape
+    code = gqa.GQA_BF16 if dtype == "bf16" else gqa.GQA_F32
+    return gqa.lib.attn_prefill_ex(None, None, None, None, 0, Hq, Hkv, 1, d, 1.0, 1, code, algo, None) == 0
 
 
 def mfma_covers(gqa, dtype, d, Hq=1, Hkv=1):
-    # a zero-size call with an explicit kernel request reports whether it covers the shape
-    code = gqa.GQA_BF16 if dtype == "bf16" else gqa.GQA_F32
-    return gqa.lib.attn_prefill_ex(None, None, None, None, 0, Hq, Hkv, 1, d, 1.0, 1, code, 2, None) == 0
+    return covers(gqa, dtype, d, ALGOS["mfma"], Hq, Hkv)
 
 
 def algos_for(dtype, d, Hq=1, Hkv=1):
+    """Every kernel that covers the shape: the vector kernel, the matrix-core kernel
+    (one workgroup per q-tile) and the bf16 split-key matrix-core kernel."""
     import grouped_query_attention_amd as gqa
     a = ["generic"]
-    if mfma_covers(gqa, dtype, d, Hq, Hkv):
-        a.append("mfma")
+    for name in ("mfma", "split"):
+        if covers(gqa, dtype, d, ALGOS[name], Hq, Hkv):
+            a.append(name)
     return a
 
 
@@ -96,6 +103,8 @@ RAGGED = [
     (1, 2, 2, 1, 32, True),      # one row: a workgroup of padding rows
     (1, 4, 1, 128, 96, True),    # exactly one 128-row tile
     (1, 2, 1, 1000, 128, True),  # many key tiles, ragged end
+    (2, 8, 4, 700, 64, True),    # split-key kernel with 4 splits per slice
+    (2, 12, 12, 900, 32, True),  # split-key kernel with 2 splits per slice
 ]
 
 

@@ -41,7 +41,7 @@ from oracle import backward as bw
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 1.5e-2}
-GENERIC, MFMA, AUTO = 1, 2, 0
+GENERIC, MFMA, AUTO, SPLIT = 1, 2, 0, 3
 SEED = si.SEED_BASE + 700
 
 
@@ -71,6 +71,8 @@ PREFILL_KERNELS = [
     ("bf16", 80, 2, 2, MFMA),     # matrix cores, one head, padded P V head dims
     ("bf16", 64, 3, 1, MFMA),     # matrix cores, odd group: one head per workgroup
     ("bf16", 128, 2, 1, GENERIC),  # vector kernel
+    ("bf16", 128, 4, 2, SPLIT),   # split-key matrix-core kernel
+    ("bf16", 80, 2, 1, SPLIT),    # split-key, padded P V head dims
     ("f32", 64, 2, 2, MFMA),      # fp32 matrix cores
     ("f32", 128, 4, 2, MFMA),     # fp32 matrix cores, two heads per workgroup
     ("f32", 48, 2, 1, MFMA),      # fp32 matrix cores, padded head dims
@@ -79,7 +81,7 @@ PREFILL_KERNELS = [
 
 
 def kid(c):
-    return "%s_d%d_Hq%d_Hkv%d_%s" % (c[0], c[1], c[2], c[3], {1: "generic", 2: "mfma", 0: "auto"}[c[4]])
+    return "%s_d%d_Hq%d_Hkv%d_%s" % (c[0], c[1], c[2], c[3], {1: "generic", 2: "mfma", 0: "auto", 3: "split"}[c[4]])
 
 
 @pytest.mark.parametrize("factor", [8, 64])
