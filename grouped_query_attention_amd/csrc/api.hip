@@ -263,6 +263,27 @@ int attn_decode_window(const void* q, const void* kcache, const void* vcache, fl
 }
 
 
+int attn_decode_cached_noalloc(const void* q, const void* kcache, const void* vcache, float* out,
+                               int newTokens, int totalLen, int startPos, int Hq, int Hkv, int d_h,
+                               int B, int dtype, void* stream) {
+  // every argument check of attn_decode_cached first: nothing touches the device for a
+  // call that will be rejected
+  int rc = decode_check(newTokens, totalLen, startPos, Hq, Hkv, d_h, B, dtype);
+  if (rc != GQA_OK) return rc;
+  if (B == 0 || newTokens == 0) return GQA_OK;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return GQA_EINVAL;
+  const size_t need = gqa::plan_decode(B, newTokens, totalLen, Hq, Hkv, d_h, dtype).workspace;
+  if (need > GQA_NOALLOC_SCRATCH_BYTES) return GQA_ESCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = gqa::noalloc_scratch(&ws);
+    if (rc != GQA_OK) return rc;
+  }
+  return decode_impl(q, kcache, vcache, out, newTokens, totalLen, startPos, Hq, Hkv, d_h, B, 0,
+                     dtype, ws, need > 0 ? GQA_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
 size_t attn_decode_paged_workspace_bytes(int B, int newTokens, int Hq, int Hkv, int d_h,
                                          int block_size, int max_blocks, int dtype) {
   return paged_ws_impl(B, newTokens, Hq, Hkv, d_h, block_size, max_blocks, 0, dtype);

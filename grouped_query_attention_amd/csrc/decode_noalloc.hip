@@ -1,6 +1,7 @@
-// decode_noalloc.hip -- attn_decode_cached_noalloc: cached decode whose split-KV partials
-// live in a fixed device array of the library instead of a caller workspace, for callers
-// that cannot allocate device memory (graph capture, tight serving loops).
+// decode_noalloc.hip -- the fixed device scratch of attn_decode_cached_noalloc (declared in
+// include/gqa_attn.h, validated and launched in api.hip): cached decode whose split-KV
+// partials live in this array instead of a caller workspace, for callers that cannot
+// allocate device memory (graph capture, tight serving loops).
 //
 // In host code the array's name below is only a host-side stand-in; its address on a
 // device comes from hipGetSymbolAddress, taken once per device (with that device
@@ -11,6 +12,7 @@
 #include <mutex>
 
 #include "gqa_attn.h"
+#include "launch.h"
 
 static __device__ __align__(256) char scratch[GQA_NOALLOC_SCRATCH_BYTES];
 
@@ -20,9 +22,13 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch[kMaxDevices];  // device address of `scratch`, per device
 std::mutex g_setup;
 
+}  // namespace
+
+namespace gqa {
+
 // Address of the current device's copy of `scratch`; looked up on the first call on
-// that device, then reused.
-int scratch_on_current_device(void** ptr) {
+// that device (with that device current), then reused.
+int noalloc_scratch(void** ptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GQA_EHIP;
   if (dev < 0 || dev >= kMaxDevices) return GQA_EUNSUPPORTED;
@@ -39,21 +45,4 @@ int scratch_on_current_device(void** ptr) {
   return GQA_OK;
 }
 
-}  // namespace
-
-extern "C" int attn_decode_cached_noalloc(const void* q, const void* kcache, const void* vcache,
-                                          float* out, int newTokens, int totalLen, int startPos,
-                                          int Hq, int Hkv, int d_h, int B, int dtype,
-                                          void* stream) {
-  // the plan depends on the shape only (0 for shapes attn_decode_cached rejects, which
-  // it then reports itself)
-  const size_t need = attn_decode_workspace_bytes(B, newTokens, totalLen, Hq, Hkv, d_h, dtype);
-  if (need > GQA_NOALLOC_SCRATCH_BYTES) return GQA_ESCRATCH;
-  void* ws = nullptr;
-  if (need > 0) {
-    const int rc = scratch_on_current_device(&ws);
-    if (rc != GQA_OK) return rc;
-  }
-  return attn_decode_cached(q, kcache, vcache, out, newTokens, totalLen, startPos, Hq, Hkv, d_h, B,
-                            dtype, ws, need > 0 ? GQA_NOALLOC_SCRATCH_BYTES : 0, stream);
-}
+}  // namespace gqa

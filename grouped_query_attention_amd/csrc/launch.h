@@ -80,6 +80,9 @@ struct DecodeArgs {
   int window;      // local window; 0 = none
 };
 hipError_t launch_attn_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+// Device address of the fixed scratch array of attn_decode_cached_noalloc on the current
+// device (GQA_NOALLOC_SCRATCH_BYTES); a gqa_status code.
+int noalloc_scratch(void** ptr);
 
 // Paged history: kc/vc of DecodeArgs are the block pools, [num_blocks, Hkv, block_size, d]
 // (head-major blocks) or [num_blocks, block_size, Hkv, d] (token_major); L and start_pos

@@ -1,11 +1,13 @@
 """Row statistics (attn_prefill_lse) and the backward pass (attn_backward) on the GPU
 against the float64 oracle (oracle/backward.py).
 
-* lse from both forward kernels (bf16 matrix cores and the fp32 vector kernel) against
+* lse from the forward kernels (bf16 matrix cores, split-key bf16 matrix cores for small
+  shapes, fp32 matrix cores, and the vector kernel for head dims those do not take) against
   the oracle's row log-sum-exp; the output is bitwise that of attn_prefill.
 * dq, dk, dv element by element against the oracle on ragged shapes (T not a multiple
   of the 32/64/128-row tiles), every head dim the matrix-core path takes (16..128 in
-  steps of 16), group sizes 1, 2, 4, causal and not, and at the full GQA prefill workload on sampled head groups.
+  steps of 16), group sizes 1, 2, 4, causal and not, and at the full GQA prefill workload on every
+  head group.
   The GPU recomputes P from bf16 Q/K, rounds P, dS and dO to bf16 for the matrix cores
   and accumulates in fp32; the bar is the bf16-input tolerance 1.5e-2 applied to the
   gradient scaled by its own size: max|gpu - ref| <= 1.5e-2 * max(1, max|ref|).

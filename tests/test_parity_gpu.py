@@ -105,6 +105,10 @@ RAGGED = [
     (1, 2, 1, 1000, 128, True),  # many key tiles, ragged end
     (2, 8, 4, 700, 64, True),    # split-key kernel with 4 splits per slice
     (2, 12, 12, 900, 32, True),  # split-key kernel with 2 splits per slice
+    (1, 4, 2, 230, 112, True),   # fp32: padded head dims with head pairs at D = 128
+    (1, 6, 2, 300, 128, True),   # group of 3: one head per workgroup
+    (1, 8, 2, 333, 128, True),   # group of 4: two head pairs share each K/V tile
+    (2, 16, 2, 257, 128, True),  # group of 8
 ]
 
 

@@ -38,6 +38,8 @@ PREFILL = [
     (1, 4, 2, 130, 64, 17, "f32"),
     (1, 2, 1, 100, 24, 10, "bf16"),
     (2, 8, 2, 2048, 128, 1000, "bf16"),
+    (1, 4, 2, 300, 128, 100, "f32"),   # fp32 matrix cores, two heads of a group per workgroup
+    (1, 4, 2, 260, 112, 70, "f32"),    # fp32 matrix cores, padded head dims, head pairs
 ]
 
 
