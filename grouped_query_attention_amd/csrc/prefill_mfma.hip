@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   constexpr int KP = G_::kKStride / 16, VP = G_::kVStride / 16, C16 = D / 8, RB = D * 2;
   constexpr int KI = (kSub * KP + kWgWaves - 1) / kWgWaves;  // wave instructions per wave per stage
   constexpr int VI = (kSub * VP + kWgWaves - 1) / kWgWaves;
-  int koff[KI], voff[VI];
+  unsigned koff[KI], voff[VI];
   bool vpad[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
@@ -199,20 +199,20 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // clamp a source offset to the last valid row of a ragged stage
-  auto clamp_row = [&](int off, int rmax) {
-    const int r = off / RB;
-    return r > rmax ? off - (r - rmax) * RB : off;
+  auto clamp_row = [&](unsigned off, int rmax) -> unsigned {
+    const int r = (int)(off / RB);
+    return r > rmax ? off - (unsigned)((r - rmax) * RB) : off;
   };
-  auto stage = [&](int t, char* dst) {
-    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kStage * RB;
-    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kStage * RB;
-    const bool ragged = t * kStage + kStage > T;
-    const int rmax = T - 1 - t * kStage;  // last valid row of this stage
+  // One stage's loads.  A stage inside T issues every load from the stage's base (an
+  // SGPR pair) plus the lane's fixed 32-bit offset, with no vector arithmetic; only a
+  // ragged last stage clamps its rows.
+  auto issue = [&](const char* kb, const char* vb, char* dst, int rmax, auto ragged_c) {
+    constexpr bool kRagged = decltype(ragged_c)::value;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int inst = wave_u + kWgWaves * i;
       if (inst < kSub * KP) {
-        const int off = ragged ? clamp_row(koff[i], rmax) : koff[i];
+        const unsigned off = kRagged ? clamp_row(koff[i], rmax) : koff[i];
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(kb + off),
             (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
@@ -222,12 +222,21 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
     for (int i = 0; i < VI; ++i) {
       const int inst = wave_u + kWgWaves * i;
       if (inst < kSub * VP && !(kOnesCol && vpad[i])) {
-        const int off = ragged ? clamp_row(voff[i], rmax) : voff[i];
+        const unsigned off = kRagged ? clamp_row(voff[i], rmax) : voff[i];
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(vb + off),
             (__attribute__((address_space(3))) void*)(dst + G_::kKTile + inst * 1024), 16, 0, 0);
       }
     }
+  };
+  auto stage = [&](int t, char* dst) {
+    const char* kb = reinterpret_cast<const char*>(kg) + (long long)t * kStage * RB;
+    const char* vb = reinterpret_cast<const char*>(vg) + (long long)t * kStage * RB;
+    // (the window instantiation keeps one load path: a second copy costs it registers)
+    if (WIN || t * kStage + kStage > T)
+      issue(kb, vb, dst, T - 1 - t * kStage, std::true_type{});
+    else
+      issue(kb, vb, dst, 0, std::false_type{});
   };
 
   // ---- per-block pieces.  The online softmax runs over 32-key blocks: a block's S^T
