@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.hip", "attn_generic.hip", "prefill_mfma.hip", "decode_mfma.hip", "kv_append.hip",
            "backward_mfma.hip", "backward_generic.hip", "prefill_f32_mfma.hip", "decode_noalloc.hip",
-           "prefill_small.hip"]
+           "prefill_small.hip", "prefill_f32_small.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.
@@ -35,6 +35,7 @@ HIPCC_FLAGS = [
 # Per-source additions.  The fp32 matrix-core prefill keeps its MFMA operands and
 # accumulators in ordinary VGPRs: in the default form the compiler copied every
 # accumulator through AGPRs around the softmax rescale (about ten copies per product).
+# (The fp32 split-key kernel measured slower in that form and keeps the default.)
 EXTRA_FLAGS = {"prefill_f32_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

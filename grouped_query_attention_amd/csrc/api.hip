@@ -15,6 +15,9 @@ constexpr long long kMaxSeq = 1LL << 30;
 // every grid is one-dimensional and decodes (batch, head) from a 32-bit block index
 constexpr long long kMaxBatchHeads = 0x7fffffffLL;
 constexpr int kCUs = 256;  // compute units of the MI355X
+// fp32: the split-key kernel when the one-workgroup-per-q-tile kernel would launch fewer
+// waves than four per SIMD (its heaviest q-tile's waves then set the time)
+constexpr long long kF32SplitBelowWaves = 4 * 4 * kCUs;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -46,8 +49,8 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
                            ? gqa::prefill_f32_mfma_supported(d_h, Hq, Hkv)
                            : gqa::prefill_mfma_supported(dtype, d_h, Hq, Hkv);
   if (algo == GQA_ALGO_MFMA && !mfma_ok) return GQA_EUNSUPPORTED;
-  // the split-key kernel: bf16, no local window
-  const bool split_ok = dtype == GQA_BF16 && mfma_ok && (window == 0 || window >= T);
+  // the split-key kernels: no local window
+  const bool split_ok = mfma_ok && (window == 0 || window >= T);
   if (algo == GQA_ALGO_MFMA_SPLIT && !split_ok) return GQA_EUNSUPPORTED;
   if (B == 0 || T == 0) return GQA_OK;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_EINVAL;
@@ -58,10 +61,13 @@ int prefill_impl(const void* q, const void* k, const void* v, float* out, int B,
   if (window >= T) window = 0;
   gqa::PrefillArgs a{q, k, v, out, B, Hq, Hkv, T, d_h, scale, causal, window, lse};
   // automatic choice: the split-key kernel when one workgroup per q-tile would leave
-  // CUs idle (fewer workgroups than the 256 CUs)
-  if (algo == GQA_ALGO_MFMA_SPLIT ||
-      (algo == GQA_ALGO_AUTO && split_ok && gqa::prefill_mfma_grid(B, Hq, Hkv, T) < kCUs))
-    return status_of(gqa::launch_attn_prefill_small(a, s));
+  // the chip short of work (bf16: fewer workgroups than the 256 CUs)
+  const bool small_grid = dtype == GQA_F32
+                              ? gqa::prefill_f32_mfma_waves(B, Hq, Hkv, T, d_h) < kF32SplitBelowWaves
+                              : gqa::prefill_mfma_grid(B, Hq, Hkv, T) < kCUs;
+  if (algo == GQA_ALGO_MFMA_SPLIT || (algo == GQA_ALGO_AUTO && split_ok && small_grid))
+    return status_of(dtype == GQA_F32 ? gqa::launch_attn_prefill_f32_small(a, s)
+                                      : gqa::launch_attn_prefill_small(a, s));
   if (algo == GQA_ALGO_MFMA || (algo == GQA_ALGO_AUTO && mfma_ok)) {
     if (dtype == GQA_F32) return status_of(gqa::launch_attn_prefill_f32_mfma(a, s));
     return status_of(gqa::launch_attn_prefill_mfma(a, s));

@@ -53,6 +53,11 @@ hipError_t launch_attn_prefill_small(const PrefillArgs& a, hipStream_t stream);
 // fp32 matrix-core prefill (the same PrefillArgs, fp32 q/k/v): d a multiple of 16, <= 128.
 bool prefill_f32_mfma_supported(int d, int Hq, int Hkv);
 hipError_t launch_attn_prefill_f32_mfma(const PrefillArgs& a, hipStream_t stream);
+// Waves prefill_f32_mfma launches for the shape.
+long long prefill_f32_mfma_waves(int B, int Hq, int Hkv, int T, int d);
+// fp32 matrix-core prefill with each 32-row slice's keys split over the waves of its
+// workgroup (no local window); same shapes as prefill_f32_mfma.
+hipError_t launch_attn_prefill_f32_small(const PrefillArgs& a, hipStream_t stream);
 
 // Split-KV decode plan, a pure function of the shape.
 struct DecodePlan {

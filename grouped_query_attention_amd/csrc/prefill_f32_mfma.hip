@@ -228,6 +228,9 @@ __global__ __launch_bounds__(kWaves * 64 * HPW) void prefill_f32_kernel(
   }
 }
 
+// two query heads per workgroup at d = 128 when the group size is even (see launch_f32)
+int f32_hpw(int Hq, int Hkv, int d) { return ((d + 31) / 32 == 4 && (Hq / Hkv) % 2 == 0) ? 2 : 1; }
+
 template <int D, int HPW>
 hipError_t launch_f32h(const PrefillArgs& a, hipStream_t stream) {
   const int nqt = (a.T + kWaves * kRows - 1) / (kWaves * kRows);
@@ -250,6 +253,11 @@ hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+long long prefill_f32_mfma_waves(int B, int Hq, int Hkv, int T, int d) {
+  const int hpw = f32_hpw(Hq, Hkv, d);
+  return (long long)((T + kWaves * kRows - 1) / (kWaves * kRows)) * (Hq / hpw) * B * kWaves * hpw;
+}
 
 bool prefill_f32_mfma_supported(int d, int Hq, int Hkv) {
   return d > 0 && d <= 128 && d % 16 == 0 && Hkv > 0 && Hq % Hkv == 0;

@@ -59,11 +59,13 @@ enum gqa_algo {
     GQA_ALGO_GENERIC = 1, /* vector-ALU kernel: any d_h in [1, 256], fp32 or bf16 */
     GQA_ALGO_MFMA = 2,    /* matrix-core kernel: bf16 with d_h a multiple of 16, <= 128, or
                              fp32 with d_h a multiple of 16, <= 128 (products in fp32) */
-    GQA_ALGO_MFMA_SPLIT = 3 /* bf16 matrix-core kernel that splits each 32-row query slice's
-                               keys over the waves of a workgroup and merges their partial
-                               softmax states exactly; same head dims as GQA_ALGO_MFMA, no
-                               local window.  GQA_ALGO_AUTO takes it when one workgroup per
-                               q-tile would give fewer workgroups than the GPU has CUs. */
+    GQA_ALGO_MFMA_SPLIT = 3 /* matrix-core kernel (bf16, or fp32 with fp32 products) that
+                               splits each 32-row query slice's keys over the waves of a
+                               workgroup and merges their partial softmax states exactly;
+                               same head dims as GQA_ALGO_MFMA, no local window.
+                               GQA_ALGO_AUTO takes it when one workgroup per q-tile would
+                               leave the GPU's CUs short of work (bf16: fewer workgroups
+                               than CUs; fp32: fewer than four waves per SIMD). */
 };
 
 /*

@@ -49,7 +49,7 @@ def mfma_covers(gqa, dtype, d, Hq=1, Hkv=1):
 
 def algos_for(dtype, d, Hq=1, Hkv=1):
     """Every kernel that covers the shape: the vector kernel, the matrix-core kernel
-    (one workgroup per q-tile) and the bf16 split-key matrix-core kernel."""
+    (one workgroup per q-tile) and the split-key matrix-core kernel."""
     import grouped_query_attention_amd as gqa
     a = ["generic"]
     for name in ("mfma", "split"):

@@ -77,6 +77,9 @@ PREFILL_KERNELS = [
     ("f32", 128, 4, 2, MFMA),     # fp32 matrix cores, two heads per workgroup
     ("f32", 48, 2, 1, MFMA),      # fp32 matrix cores, padded head dims
     ("f32", 40, 2, 1, GENERIC),   # vector kernel
+    ("f32", 64, 2, 2, SPLIT),     # fp32 split-key matrix-core kernel
+    ("f32", 48, 2, 1, SPLIT),     # fp32 split-key, padded head dims
+    ("f32", 128, 4, 2, SPLIT),    # fp32 split-key at the largest head dim
 ]
 
 
