@@ -474,10 +474,13 @@ __global__ __launch_bounds__(kWgWaves * 64, 2) void prefill_mfma_kernel(
       *reinterpret_cast<u32x4*>(base) = val;
     }
   }
+  // the first stage alone before the first barrier: at launch every workgroup's first
+  // loads come from HBM at once, and the second stage is in flight during the first's
+  // compute either way
   stage(t0, lds_a);
-  if (t0 + 1 < nstages) stage(t0 + 1, lds_b);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (t0 + 1 < nstages) stage(t0 + 1, lds_b);
   for (int t = t0; t < nstages; t += 2) {
     step(t, lds_a);
     if (t + 1 < nstages) step(t + 1, lds_b);
