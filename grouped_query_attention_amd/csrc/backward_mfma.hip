@@ -498,40 +498,49 @@ __global__ __launch_bounds__(kQWaves * 64, 2) void bwd_dq_kernel(
     }
   };
 
-  // A stage all of whose keys are visible to every row of this wave: both 32-key blocks
-  // in straight-line code (the second block's products beside the first block's vector
-  // work, as in the dK/dV kernel).
-  auto compute_fast = [&](const char* buf) __attribute__((always_inline)) {
-    f32x16 s[2], dp[2];
+  // A stage all of whose keys are visible to every row of this wave: its 32-key blocks
+  // as one software pipeline in straight-line code -- block b+1's S^T and dP^T products,
+  // block b's exp and dS vector work and block b-1's dQ products are independent, so the
+  // matrix cores and the vector ALU overlap inside the wave.
+  auto sdp = [&](const char* buf, int blk, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    s = f32x16{};
+    dp = f32x16{};
+    const SwzRow krow(buf + (32 * blk + col) * TS, col, half);
+    const char* vrow = buf + kKT + (32 * blk + col) * RS + half * 16;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16{};
-      dp[blk] = f32x16{};
-      const SwzRow krow(buf + (32 * blk + col) * TS, col, half);
-      const char* vrow = buf + kKT + (32 * blk + col) * RS + half * 16;
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(krow.frag(st), qf[st], s[blk], 0, 0, 0);
-        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(vrow + st * 32), of[st], dp[blk], 0, 0, 0);
-      }
+    for (int st = 0; st < KS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(krow.frag(st), qf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_row_frag(vrow + st * 32), of[st], dp, 0, 0, 0);
     }
+  };
+  auto soft = [&](const f32x16& s, const f32x16& dp, bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+      sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dq));
+    }
+  };
+  auto dqp = [&](const char* buf, int blk, const bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const char* kt16 = buf + (32 * blk + 16 * kk) * TS;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<D>(kt16, lane, db), sb[kk], dqa[db], 0, 0, 0);
+    }
+  };
+  auto compute_fast = [&](const char* buf) __attribute__((always_inline)) {
+    constexpr int NB = kKStage / 32;
+    f32x16 s[2], dp[2];
     bf16x8 sb[2][2];
+    sdp(buf, 0, s[0], dp[0]);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -l2));
-        sb[blk][r >> 3][r & 7] = (__bf16)(p * (dp[blk][r] - Dq));
-      }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const char* kt16 = buf + (32 * blk + 16 * kk) * TS;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_tr_frag<D>(kt16, lane, db), sb[blk][kk], dqa[db], 0, 0, 0);
-      }
+    for (int blk = 0; blk < NB; ++blk) {
+      if (blk + 1 < NB) sdp(buf, blk + 1, s[(blk + 1) & 1], dp[(blk + 1) & 1]);
+      soft(s[blk & 1], dp[blk & 1], sb[blk & 1]);
+      if (blk >= 1) dqp(buf, blk - 1, sb[(blk - 1) & 1]);
+    }
+    dqp(buf, NB - 1, sb[(NB - 1) & 1]);
   };
   auto run = [&](int t, const char* buf) __attribute__((always_inline)) {
     const int j0 = t * kKStage;

@@ -70,9 +70,11 @@ def test_window_one_is_own_value(gqa, d):
     assert torch.equal(out.cpu(), want)
 
 
-@pytest.mark.parametrize("d", [128, 80])
-def test_wide_window_is_causal_bitwise(gqa, d):
-    q, k, v = si.prefill_inputs(1, 4, 2, 333, d, "bf16", seed=3300 + d)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 80), ("f32", 128), ("f32", 48)])
+def test_wide_window_is_causal_bitwise(gqa, dtype, d):
+    # a window reaching key 0 from every row takes the causal call's kernel (at this
+    # small shape the split-key kernel, in either dtype)
+    q, k, v = si.prefill_inputs(1, 4, 2, 333, d, dtype, seed=3300 + d)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
     a = gqa.attn_prefill(qc, kc, vc, scale=d ** -0.5)
     for W in (333, 334, 100000):
