@@ -4,7 +4,8 @@
   T=8192, d=128, causal), bf16 and fp32 inputs, on the one-workgroup-per-q-tile kernels
   (the automatic choice at this size).
 * Cached decode over a cache of 2^32 elements per tensor (64 sequences, 8 K/V heads,
-  65536 positions, d=128, bf16), newTokens 1.
+  65536 positions, d=128, bf16), newTokens 1; then the same history scattered in
+  16-position blocks over a pool of the same size, through the paged call.
 
 The inputs are seeded N(0,1) draws made on the device (host memory would need tens of
 GB).  Sampled output rows at the far end of the tensors, the very last one included,
@@ -17,6 +18,7 @@ import pytest
 import torch
 
 import oracle
+import seeded_inputs as si
 
 pytestmark = pytest.mark.gpu
 
@@ -87,5 +89,14 @@ def test_decode_past_2g_elements(gqa):
                                     nthreads=max(1, min(16, os.cpu_count() or 1)))
         err = float(np.abs(out[b:b + 1].cpu().double().numpy() - want).max())
         assert err <= TOL["bf16"], (b, err)
-    del kc, vc, q, out
+    # the same history in 16-position blocks of a pool of 2^32 elements per tensor, in
+    # seeded random order: the paged call reads the same rows, so it is bitwise the same
+    kp, vp, table, lens = si.paged_from_contiguous(kc, vc, 16, SEED + 6)
+    del kc, vc
+    torch.cuda.empty_cache()
+    print("paged decode over a pool of %d blocks" % kp.shape[0], flush=True)
+    paged = gqa.attn_decode_paged(q, kp, vp, table, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(paged, out)
+    del kp, vp, q, out, paged
     torch.cuda.empty_cache()
