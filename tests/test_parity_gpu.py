@@ -109,6 +109,8 @@ RAGGED = [
     (1, 6, 2, 300, 128, True),   # group of 3: one head per workgroup
     (1, 8, 2, 333, 128, True),   # group of 4: two head pairs share each K/V tile
     (2, 16, 2, 257, 128, True),  # group of 8
+    (1, 10, 2, 150, 48, True),   # group of 5, head dim 16 mod 32
+    (2, 5, 1, 66, 112, False),   # odd head count sharing one K/V head, full attention
 ]
 
 
